@@ -1,0 +1,280 @@
+"""Float64 CPU oracle of exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY -- never imported by the product path.
+
+Sources (web pages on IO-aware exact attention; cited by title and section):
+  [FAQ-short] "Walk through what FlashAttention does differently from standard
+              attention, and what changes between v1, v2, and v3" (zenaique.com,
+              attn-flashattention-family-shortans-hard): answer paragraphs 1-2.
+  [Card]      "FlashAttention Kernel & Online Softmax" (talentme.airsota.com
+              mind-map card): definition paragraph, history paragraph, prompts.
+  [Blog]      "FlashAttention" (akshathtiwari.co.in/blog/flashattention): the
+              explainer paragraph (online softmax with m, ell and O; recompute
+              in the backward pass).
+  [FAQ-mcq]   "What does FlashAttention v1 actually change vs standard
+              attention?" (zenaique.com, attn-flashattention-family-mcq-hard):
+              answer, the online-softmax code figure, the version table.
+
+What is computed. All pages agree that the tiled method returns the result of
+the textbook formula Attn(Q,K,V) = softmax(Q K^T / sqrt(d)) V exactly, with
+only floating-point rounding differing ([FAQ-short] answer paragraphs 1-2,
+[Blog], [FAQ-mcq] answer). So this oracle is that formula written out: it
+materialises the full score matrix in float64 and never tiles, fuses or
+reorders anything.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * scale: passed explicitly (the configurations use 1/sqrt(d)); the float64
+    value of the float32 scale argument multiplies Q K^T.
+  * causal: key j is visible to query i iff j <= i (lower-triangular mask).
+  * logsumexp: lse_i = m_i + ln(l_i) over the *scaled* scores, natural log --
+    the pages save the running max m and denominator l for the backward pass
+    ([FAQ-short] answer paragraph 2; [FAQ-mcq] answer "tile + save m,l");
+    their log-sum is one number per row carrying both.
+  * backward: the pages only say that the backward pass recomputes the score
+    blocks from Q, K, V and the saved statistics ([FAQ-short] paragraph 2,
+    [Card] history paragraph, [Blog]); the gradients themselves are the
+    textbook softmax Jacobian of <O, dO>, written out in `backward`.
+  * fp8 inputs: the path multiplies E4M3 codes by per-tensor float32 scales;
+    the oracle works on the dequantised values code * scale, which float64
+    holds exactly.
+"""
+import math
+
+import numpy as np
+
+__all__ = [
+    "scores", "probabilities", "forward", "forward_quantized", "backward",
+    "online_softmax_chunked", "brute_force_forward", "brute_force_backward",
+    "decode_e4m3fn",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def scores(q, k, scale, causal, rows=None):
+    """Scaled scores S = c * Q K^T for one head, masked.
+
+    q: [Nq, d] (all rows, or the rows listed in `rows`), k: [Nk, d].
+    rows: optional 1-D index array; the query positions the rows of `q`
+          stand for (needed for the causal mask when only a sample of rows
+          is computed). Default: 0..Nq-1.
+    Masked entries are -inf. Definition: [FAQ-short] answer paragraph 1
+    (the softmax argument Q K^T / sqrt(d_k)); [Card] definition paragraph
+    (S = Q K^T / sqrt(d)).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    c = float(np.float32(scale))
+    s = c * (q @ k.T)
+    if causal:
+        qi = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+        kj = np.arange(k.shape[0])
+        s = np.where(kj[None, :] <= qi[:, None], s, -np.inf)
+    return s
+
+
+def _softmax_rows(s):
+    """Row softmax with the max subtracted; returns (P, m, l)."""
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=1, keepdims=True)
+    return e / l, m[:, 0], l[:, 0]
+
+
+def probabilities(q, k, scale, causal):
+    """Full attention matrix P = softmax(S) of one head (rows sum to 1)."""
+    p, _, _ = _softmax_rows(scores(q, k, scale, causal))
+    return p
+
+
+def forward(q, k, v, scale, causal, rows=None):
+    """O = softmax(c Q K^T) V and lse for tensors laid out [B, H, N, d].
+
+    rows: None for every query row, or an int array [B, H, R] of query
+          positions (each row is computed against all keys and masked
+          causally by its own position).
+    Returns (O [B,H,R,d], lse [B,H,R]) in float64, lse = m + ln(l) with
+    m = max_j S_ij and l = sum_j exp(S_ij - m).
+    Definition: [FAQ-short] answer paragraph 1, [Card] definition paragraph.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, H, N, d = q.shape
+    R = N if rows is None else np.asarray(rows).shape[-1]
+    out = np.empty((B, H, R, v.shape[-1]))
+    lse = np.empty((B, H, R))
+    for b in range(B):
+        for h in range(H):
+            idx = None if rows is None else np.asarray(rows)[b, h]
+            qh = q[b, h] if idx is None else q[b, h][idx]
+            p, m, l = _softmax_rows(scores(qh, k[b, h], scale, causal, idx))
+            out[b, h] = p @ v[b, h]
+            lse[b, h] = m + np.log(l)
+    return out, lse
+
+
+def decode_e4m3fn(codes):
+    """Decode OCP FP8 E4M3 ("fn": no infinities) bytes to float64.
+
+    Format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 is subnormal (mantissa * 2^-9); S.1111.111 is NaN;
+    largest finite magnitude 448. This is the E4M3 format the pages name for
+    the FP8 path ([FAQ-short] answer paragraph 2; [FAQ-mcq] version table).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    mant = c & 0x7
+    normal = sign * (1.0 + mant / 8.0) * np.exp2(e - 7.0)
+    sub = sign * mant * 2.0 ** -9
+    val = np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def forward_quantized(qc, kc, vc, sq, sk, sv, scale, causal, rows=None):
+    """Attention of per-tensor-scaled FP8 E4M3 inputs.
+
+    qc, kc, vc: uint8 E4M3 codes [B,H,N,d]; sq, sk, sv: the float32
+    per-tensor scales. The inputs the path sees are code * scale, so the
+    oracle is `forward` on exactly those values (float64 holds each product
+    exactly: 4 significant bits times 24).
+    """
+    q = decode_e4m3fn(qc) * float(np.float32(sq))
+    k = decode_e4m3fn(kc) * float(np.float32(sk))
+    v = decode_e4m3fn(vc) * float(np.float32(sv))
+    return forward(q, k, v, scale, causal, rows)
+
+
+def backward(q, k, v, do, scale, causal, heads=None):
+    """Gradients of <O, dO> with respect to Q, K, V ([B,H,N,d] tensors).
+
+    The pages state only that the backward pass recomputes P from Q, K, V
+    and the saved statistics instead of storing it ([FAQ-short] paragraph 2,
+    [Card] history paragraph, [Blog]). The gradient formulas are the
+    textbook chain rule through O = P V and the row softmax:
+        dV = P^T dO
+        dP = dO V^T
+        D_i = sum_j P_ij dP_ij
+        dS = P * (dP - D)          (softmax Jacobian, row by row)
+        dQ = c dS K,  dK = c dS^T Q
+    heads: optional list of (b, h) pairs; others are left as NaN.
+    Returns (dQ, dK, dV) float64.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    c = float(np.float32(scale))
+    B, H, N, d = q.shape
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in pairs:
+        p = probabilities(q[b, h], k[b, h], scale, causal)
+        dv[b, h] = p.T @ do[b, h]
+        dp = do[b, h] @ v[b, h].T
+        dd = np.sum(p * dp, axis=1, keepdims=True)
+        ds = p * (dp - dd)
+        dq[b, h] = c * (ds @ k[b, h])
+        dk[b, h] = c * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def online_softmax_chunked(s_row, v_rows, bounds):
+    """Streaming softmax of one score row over chunks, with values.
+
+    The pages' chunked online softmax ([FAQ-mcq] code figure) keeps a
+    running max m and denominator l and rescales them by exp(m - m_new) per
+    chunk; its value numerator is left as a comment there, and is completed
+    here the way [Blog] states it: the running output accumulator O is
+    rescaled by the same factor and the chunk's exp(s - m_new) * v terms are
+    added; after the last chunk O / l is the softmax-weighted output ([Card]
+    definition paragraph: normalise by 1/l at the end).
+
+    s_row: [n] scores (may hold -inf for masked keys); v_rows: [n, d];
+    bounds: chunk edges 0 = b0 < b1 < ... < bK = n.
+    A chunk whose scores are all -inf while m is still -inf contributes
+    nothing (the figure's exp(m - m_new) would be exp(-inf + inf)); that
+    guard is the plain reading that such a chunk holds no mass.
+    Returns (m, l, O / l).
+    """
+    s_row = _f64(s_row)
+    v_rows = _f64(v_rows)
+    m = -math.inf
+    l = 0.0
+    acc = np.zeros(v_rows.shape[1])
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        chunk = s_row[lo:hi]
+        m_new = max(m, float(np.max(chunk)))
+        if m_new == -math.inf:
+            continue
+        corr = math.exp(m - m_new)
+        w = np.exp(chunk - m_new)
+        l = l * corr + float(np.sum(w))
+        acc = acc * corr + w @ v_rows[lo:hi]
+        m = m_new
+    return m, l, acc / l
+
+
+def _bf_scores(q, k, c, causal):
+    n, nk = len(q), len(k)
+    s = [[-math.inf] * nk for _ in range(n)]
+    for i in range(n):
+        for j in range(nk):
+            if not causal or j <= i:
+                s[i][j] = c * math.fsum(q[i][t] * k[j][t] for t in range(len(q[i])))
+    return s
+
+
+def _bf_softmax(s):
+    p = []
+    for row in s:
+        m = max(row)
+        e = [math.exp(x - m) for x in row]
+        tot = math.fsum(e)
+        p.append([x / tot for x in e])
+    return p
+
+
+def brute_force_forward(q, k, v, scale, causal):
+    """Pure-Python single-head forward with math.fsum (tiny N only).
+
+    q, k, v: nested lists / arrays [N, d]. Returns (O, lse) as lists.
+    """
+    c = float(np.float32(scale))
+    q, k, v = [[float(x) for x in r] for r in q], [[float(x) for x in r] for r in k], [[float(x) for x in r] for r in v]
+    s = _bf_scores(q, k, c, causal)
+    p = _bf_softmax(s)
+    o = [[math.fsum(p[i][j] * v[j][t] for j in range(len(v))) for t in range(len(v[0]))] for i in range(len(q))]
+    lse = []
+    for row in s:
+        m = max(row)
+        lse.append(m + math.log(math.fsum(math.exp(x - m) for x in row)))
+    return o, lse
+
+
+def brute_force_backward(q, k, v, do, scale, causal):
+    """Pure-Python single-head backward with math.fsum (tiny N only).
+
+    Written element by element from the chain rule:
+      dV_jt = sum_i P_ij dO_it
+      dS_ij = P_ij (sum_t dO_it V_jt - sum_j' P_ij' sum_t dO_it V_j't)
+      dQ_it = c sum_j dS_ij K_jt ;  dK_jt = c sum_i dS_ij Q_it
+    """
+    c = float(np.float32(scale))
+    q, k, v, do = ([[float(x) for x in r] for r in t] for t in (q, k, v, do))
+    n, nk, d = len(q), len(k), len(q[0])
+    p = _bf_softmax(_bf_scores(q, k, c, causal))
+    dv = [[math.fsum(p[i][j] * do[i][t] for i in range(n)) for t in range(d)] for j in range(nk)]
+    dp = [[math.fsum(do[i][t] * v[j][t] for t in range(d)) for j in range(nk)] for i in range(n)]
+    ds = []
+    for i in range(n):
+        dd = math.fsum(p[i][j] * dp[i][j] for j in range(nk))
+        ds.append([p[i][j] * (dp[i][j] - dd) for j in range(nk)])
+    dq = [[c * math.fsum(ds[i][j] * k[j][t] for j in range(nk)) for t in range(d)] for i in range(n)]
+    dk = [[c * math.fsum(ds[i][j] * q[i][t] for i in range(n)) for t in range(d)] for j in range(nk)]
+    return dq, dk, dv

@@ -1,0 +1,55 @@
+"""Planted mistakes in copies of the oracle must each fail some pin.
+
+Each mutant is the oracle's source with one plausible slip (a dropped term,
+a wrong sign or index, a transposed operand, an off-by-one mask, a wrong
+exponent bias), executed as a separate module on the CPU. The pins are the
+ones the real oracle passes, so a mutant that passed them all would show a
+blind spot in the pins.
+"""
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "oracle", "attention.py")).read()
+
+MUTANTS = {
+    "scale_dropped": ("s = c * (q @ k.T)", "s = (q @ k.T)"),
+    "causal_off_by_one": ("kj[None, :] <= qi[:, None]", "kj[None, :] < qi[:, None]"),
+    "causal_flipped": ("kj[None, :] <= qi[:, None]", "kj[None, :] >= qi[:, None]"),
+    "no_max_shift_lse": ("lse[b, h] = m + np.log(l)", "lse[b, h] = np.log(l)"),
+    "lse_log2": ("lse[b, h] = m + np.log(l)", "lse[b, h] = m + np.log2(l)"),
+    "pv_transposed_in_dv": ("dv[b, h] = p.T @ do[b, h]", "dv[b, h] = p @ do[b, h]"),
+    "missing_D_term": ("ds = p * (dp - dd)", "ds = p * dp"),
+    "dk_scale_dropped": ("dk[b, h] = c * (ds.T @ q[b, h])", "dk[b, h] = (ds.T @ q[b, h])"),
+    "dq_uses_q": ("dq[b, h] = c * (ds @ k[b, h])", "dq[b, h] = c * (ds @ q[b, h])"),
+    "dp_sign": ("dp = do[b, h] @ v[b, h].T", "dp = -(do[b, h] @ v[b, h].T)"),
+    "online_no_rescale": ("acc = acc * corr + w @ v_rows[lo:hi]", "acc = acc + w @ v_rows[lo:hi]"),
+    "online_l_no_rescale": ("l = l * corr + float(np.sum(w))", "l = l + float(np.sum(w))"),
+    "e4m3_bias8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    "e4m3_subnormal": ("sub = sign * mant * 2.0 ** -9", "sub = sign * mant * 2.0 ** -10"),
+    "softmax_no_normalise": ("return e / l, m[:, 0], l[:, 0]", "return e, m[:, 0], l[:, 0]"),
+    "dequant_scale_dropped": ("q = decode_e4m3fn(qc) * float(np.float32(sq))", "q = decode_e4m3fn(qc)"),
+}
+
+
+def _load(name, old, new):
+    assert SRC.count(old) == 1, f"mutant {name}: pattern not found exactly once"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(SRC.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load(name, *MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError, or a crash caused by the slip
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches mutant {name}"
