@@ -1,0 +1,119 @@
+/*
+ * fa.h -- C ABI of the exact IO-aware attention library (libfa.so, gfx950).
+ *
+ * Operation. Exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * per (batch, head), as defined on the page "Walk through what
+ * FlashAttention does differently from standard attention ..." (zenaique.com,
+ * FlashAttention family short answer), answer paragraph 1, and on the card
+ * "FlashAttention Kernel & Online Softmax", definition paragraph. The library
+ * computes it tile by tile with an online softmax (running max, running
+ * denominator, rescaled output accumulator; same card, definition paragraph;
+ * "FlashAttention" explainer by A. Tiwari) so that no N x N matrix is ever
+ * written to device memory. The forward pass saves O and one log-sum-exp
+ * per row (the pages save the running max m and denominator l; here
+ * lse = m + ln l over the scaled scores, natural log). The backward pass
+ * recomputes the score blocks from Q, K, V and lse (short-answer page,
+ * answer paragraph 2; card, history paragraph).
+ *
+ * Conventions common to every entry point:
+ *   - Tensors are dense, row-major [B, H, N, d] (d fastest), 16-byte
+ *     aligned; lse and the backward workspace are [B, H, N] float32.
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The
+ *     library never allocates or frees device memory and keeps no state
+ *     between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and is asynchronous. The return value reports argument
+ *     validation and launch errors only; a device fault surfaces at the
+ *     caller's next synchronisation. On a non-zero return nothing has been
+ *     launched and no output has been written.
+ *   - Supported head sizes: d = 64 or d = 128. Any N >= 1 (ragged tails are
+ *     masked). B = 0 or H = 0 is a no-op that returns FA_OK.
+ *   - causal != 0 applies the lower-triangular mask: key j is visible to
+ *     query i iff j <= i.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum  */
+  FA_ERR_UNSUPPORTED = -2, /* head size or dtype combination not built   */
+  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  FA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch   */
+} fa_status;
+
+typedef enum {
+  FA_F32 = 0,      /* IEEE float32                                       */
+  FA_BF16 = 1,     /* bfloat16                                           */
+  FA_FP8_E4M3 = 3  /* OCP FP8 E4M3 ("fn": finite only, max 448), inputs only */
+} fa_dtype;
+
+/*
+ * fa_forward -- bf16 forward.
+ *   q, k, v : bf16 [B,H,N,d] inputs.
+ *   o       : bf16 [B,H,N,d] output, fully overwritten.
+ *   lse     : float32 [B,H,N] output, lse_i = ln sum_j exp(scale * q_i.k_j)
+ *             over the visible keys.
+ *   scale   : multiplier of Q K^T (1/sqrt(d) for standard attention).
+ * Same as fa_forward_typed(FA_BF16, FA_BF16, ..., descale = NULL, ...).
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_forward_typed -- forward with a choice of operand and output dtype.
+ *   in_dtype : FA_F32 (float32 operands, P kept float32),
+ *              FA_BF16 (bf16 operands, P rounded to bf16 for P.V),
+ *              FA_FP8_E4M3 (E4M3 codes; P quantised to E4M3 for P.V; the
+ *              FP8 path of the version table on the FlashAttention-family
+ *              multiple-choice page).
+ *   o_dtype  : FA_F32 or FA_BF16 (FA_F32 with FA_FP8_E4M3 is unsupported).
+ *   descale  : FA_FP8_E4M3 only: DEVICE pointer to 3 float32 per-tensor
+ *              scales {s_q, s_k, s_v}; the inputs stand for code * s.
+ *              Must be NULL for the other dtypes.
+ * Accumulation is float32 for every dtype; the softmax runs in float32 and
+ * the denominator is summed from the unrounded float32 probabilities.
+ */
+int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
+                     const float* descale, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, void* stream);
+
+/*
+ * fa_backward_workspace_bytes -- device workspace that fa_backward needs:
+ * one float32 per row (D_i = sum_t dO_it O_it), rounded up to 256 bytes.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_backward -- gradients of <O, dO> with respect to Q, K, V.
+ *   q, k, v, dO : bf16 [B,H,N,d].
+ *   o           : [B,H,N,d] output of the forward pass, dtype o_dtype
+ *                 (FA_F32 or FA_BF16; FA_F32 is the accurate choice because
+ *                 D = rowsum(dO * O) is formed from it).
+ *   lse         : float32 [B,H,N] from the same forward call.
+ *   dq, dk, dv  : float32 [B,H,N,d] outputs, fully overwritten.
+ *   workspace   : device buffer of at least fa_backward_workspace_bytes().
+ * The probabilities are recomputed block by block from Q, K and lse; no
+ * N x N buffer exists at any time.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                const void* dO, const float* lse, float* dq, float* dk, float* dv,
+                void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                float scale, int causal, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

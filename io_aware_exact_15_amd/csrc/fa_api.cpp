@@ -1,0 +1,90 @@
+// C ABI of the attention library: argument validation, then dispatch to the
+// kernel launchers. No allocation, no state, no exceptions across the ABI.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared shape checks. Returns FA_OK, or the status to report.
+int check_shape(int B, int H, int N, int d, float scale) {
+  if (B < 0 || H < 0 || N < 1) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // grid = B*H*ceil(N/32) must fit in an int; element offsets use size_t.
+  const long long bh = (long long)B * H;
+  if (bh > 0 && bh * ((N + 31) / 32) > INT_MAX) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head size or dtype not supported";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
+                     const float* descale, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, void* stream) {
+  int st = check_shape(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (in_dtype != FA_F32 && in_dtype != FA_BF16 && in_dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (in_dtype == FA_FP8_E4M3) {
+    if (o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!descale) return FA_ERR_INVALID_ARG;
+  } else if (descale) {
+    return FA_ERR_INVALID_ARG;
+  }
+  if ((long long)B * H == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  return fa::launch_forward(in_dtype, o_dtype, q, k, v, descale, o, lse, B, H, N, d, scale, causal,
+                            (hipStream_t)stream);
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+               int d, float scale, int causal, void* stream) {
+  return fa_forward_typed(FA_BF16, FA_BF16, q, k, v, nullptr, o, lse, B, H, N, d, scale, causal, stream);
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
+                const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, float scale, int causal, void* stream) {
+  int st = check_shape(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d) || !aligned16(workspace))
+    return FA_ERR_WORKSPACE;
+  return fa::launch_backward(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, (float*)workspace, B, H, N, d, scale,
+                             causal, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Device-side building blocks shared by the attention kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, wave64):
+//   A operand (32 x 16): lane l holds A[l % 32][8 * (l / 32) + 0..7]
+//   B operand (16 x 32): lane l holds B[8 * (l / 32) + 0..7][l % 32]
+//   C/D (32 x 32, 16 floats): lane l, register i holds
+//       C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32]
+// The contraction index only has to be assigned consistently between A and
+// B, which the kernels exploit to feed accumulator registers straight back
+// into the next product without moving data between lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// E4M3 x E4M3, K = 64: lane l holds 32 codes of row/column l % 32; the two
+// half-waves hold the two halves of the contraction.
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16). Within each
+// group of 16 lanes, lane j supplies the address of 4 consecutive elements
+// (row j / 4, columns 4 * (j % 4) .. + 3 of a 4 x 16 block); lane n then
+// receives column n of that block, one element per row.
+__device__ __forceinline__ s16x4 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 FA_LDS*)(p));
+}
+
+// Transposing LDS read of 8-bit data (ds_read_b64_tr_b8): within each group
+// of 16 lanes, lane j supplies the address of 8 consecutive bytes (row
+// j / 2, columns 8 * (j % 2) .. + 7 of an 8 x 16 block); lane n receives
+// column n, one byte per row.
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 FA_LDS*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat4(s16x4 lo, s16x4 hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Value held by the partner lane in the other half-wave (lane ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+}  // namespace fa

@@ -1,0 +1,20 @@
+// Internal entry points between the C ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+// Forward launch; arguments already validated by the ABI layer.
+int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
+                   const float* descale, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, hipStream_t stream);
+
+// Backward launch; arguments already validated by the ABI layer.
+int launch_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                    const void* dO, const float* lse, float* dq, float* dk, float* dv,
+                    float* delta, int B, int H, int N, int d, float scale, int causal,
+                    hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,99 @@
+"""Seeded synthetic workloads for the attention path.
+
+This module only draws inputs: normal samples, their casts to the operand
+dtype, the per-tensor FP8 quantisation that the FP8 workload prescribes, and
+seeded samples of query rows. It holds none of the attention arithmetic and
+serves both the GPU path and the float64 oracle, which never import each
+other.
+
+Recipe (the five workloads of the exact-attention path):
+  * Q, K, V (and dO for the backward workload), in that order, are
+    `torch.randn(B, H, N, d, dtype=float32)` from one CPU generator seeded
+    with the workload's seed, then cast to the operand dtype (bf16: round to
+    nearest even) or quantised to FP8 E4M3 with a per-tensor scale
+    s = amax|x| / 448 and codes e4m3fn(x / s) rounded to nearest even.
+  * Sampled rows: per (b, h), `sorted(default_rng([seed, b, h]).choice(N,
+    size, replace=False))`.
+"""
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+
+# name -> workload description (sizes as in the exact-attention workloads)
+WORKLOADS = {
+    "fwd_f32_b1h1_n256_d64": dict(seed=1, B=1, H=1, N=256, d=64, dtype="f32", causal=(False,),
+                                  sample=None, backward=False),
+    "fwd_bf16_b4h16_n2048_d64": dict(seed=2, B=4, H=16, N=2048, d=64, dtype="bf16", causal=(False, True),
+                                     sample=None, backward=False),
+    "fwd_bf16_causal_b1h32_n16384_d128": dict(seed=3, B=1, H=32, N=16384, d=128, dtype="bf16", causal=(True,),
+                                              sample=512, backward=False),
+    "bwd_bf16_causal_b2h16_n4096_d128": dict(seed=4, B=2, H=16, N=4096, d=128, dtype="bf16", causal=(True,),
+                                             sample=None, backward=True),
+    "fwd_fp8_causal_b1h8_n65536_d128": dict(seed=5, B=1, H=8, N=65536, d=128, dtype="fp8", causal=(True,),
+                                            sample=256, backward=False),
+}
+
+
+def normal_tensors(B, H, N, d, seed, count=3):
+    """`count` float32 N(0,1) tensors [B,H,N,d] drawn in order from one seeded CPU generator."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    return [torch.randn(B, H, N, d, dtype=torch.float32, generator=g) for _ in range(count)]
+
+
+def quantize_e4m3(x):
+    """Per-tensor FP8 E4M3 quantisation: returns (codes float8_e4m3fn, scale float32).
+
+    scale = amax|x| / 448 in float32; codes = e4m3fn(x / scale), round to
+    nearest even (torch's cast). The dequantised value is codes * scale.
+    """
+    x = x.to(torch.float32)
+    amax = x.abs().max()
+    scale = (amax / E4M3_MAX).to(torch.float32)
+    if float(scale) == 0.0:
+        scale = torch.tensor(1.0, dtype=torch.float32)
+    codes = (x / scale).to(torch.float8_e4m3fn)
+    return codes, np.float32(scale.item())
+
+
+def make_inputs(B, H, N, d, seed, dtype, with_do=False):
+    """Seeded CPU inputs of one workload.
+
+    dtype: "f32" | "bf16" | "fp8". Returns a dict with q, k, v (and do) as
+    CPU tensors of the operand dtype; for "fp8" also the scales sq, sk, sv.
+    """
+    xs = normal_tensors(B, H, N, d, seed, 4 if with_do else 3)
+    names = ["q", "k", "v", "do"][: len(xs)]
+    out = {}
+    if dtype == "f32":
+        out.update(zip(names, xs))
+    elif dtype == "bf16":
+        out.update((n, x.to(torch.bfloat16)) for n, x in zip(names, xs))
+    elif dtype == "fp8":
+        for n, x in zip(names, xs):
+            if n == "do":
+                out[n] = x.to(torch.bfloat16)
+                continue
+            codes, s = quantize_e4m3(x)
+            out[n] = codes
+            out["s" + n] = s
+    else:
+        raise ValueError(f"unknown dtype {dtype}")
+    return out
+
+
+def sample_rows(seed, B, H, N, size):
+    """Seeded query-row sample [B, H, size] (sorted, without replacement, per head)."""
+    size = min(size, N)
+    rows = np.empty((B, H, size), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            rows[b, h] = np.sort(np.random.default_rng([seed, b, h]).choice(N, size, replace=False))
+    return rows
+
+
+def to_numpy(t):
+    """CPU tensor -> numpy array that the oracle reads (exact for f32/bf16; uint8 codes for fp8)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.to(torch.float32).numpy()

@@ -1,0 +1,78 @@
+"""Helpers for GPU-vs-oracle parity: run the HIP path through the C ABI and
+compare with the float64 oracle element by element.
+
+Tolerances (absolute, over every compared element):
+  float32 operands: max |err| <= 1e-5
+  bf16 operands:    max |err| <= 1e-2 and RMS <= 2e-3
+  fp8 E4M3:         max |err| <= 6e-2
+  log-sum-exp:      max |err| <= 1e-3 (every dtype)
+"""
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from io_aware_exact_15_amd import binding as fa
+from io_aware_exact_15_amd import inputs
+
+TOL = {"f32": dict(max=1e-5, rms=None), "bf16": dict(max=1e-2, rms=2e-3), "fp8": dict(max=6e-2, rms=None)}
+LSE_TOL = 1e-3
+FA_DT = {"f32": fa.FA_F32, "bf16": fa.FA_BF16, "fp8": fa.FA_FP8_E4M3}
+
+
+def gpu_forward(inp, dtype, causal, o_dtype="bf16", scale=None):
+    """Runs fa_forward_typed on device copies of the CPU inputs; returns CPU (o float64, lse float64)."""
+    q = inp["q"]
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (inp[n].to(dev) for n in ("q", "k", "v"))
+    odt = torch.bfloat16 if o_dtype == "bf16" else torch.float32
+    o = torch.empty(B, H, N, d, dtype=odt, device=dev)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    descale = None
+    if dtype == "fp8":
+        descale = torch.tensor([inp["sq"], inp["sk"], inp["sv"]], dtype=torch.float32, device=dev)
+    fa.fa_forward_typed(FA_DT[dtype], FA_DT[o_dtype], qd, kd, vd, descale, o, lse, scale, causal)
+    torch.cuda.synchronize()
+    return o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+def oracle_forward(inp, dtype, causal, rows=None, scale=None):
+    d = inp["q"].shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if dtype == "fp8":
+        return oracle.forward_quantized(inputs.to_numpy(inp["q"]), inputs.to_numpy(inp["k"]), inputs.to_numpy(inp["v"]),
+                                        inp["sq"], inp["sk"], inp["sv"], scale, causal, rows)
+    return oracle.forward(inputs.to_numpy(inp["q"]), inputs.to_numpy(inp["k"]), inputs.to_numpy(inp["v"]),
+                          scale, causal, rows)
+
+
+def gather_rows(x, rows):
+    """x: [B,H,N,...] -> [B,H,R,...] at rows [B,H,R]."""
+    B, H = rows.shape[:2]
+    return np.stack([np.stack([x[b, h][rows[b, h]] for h in range(H)]) for b in range(B)])
+
+
+def errors(got, ref):
+    diff = np.abs(got - ref)
+    return float(diff.max()) if diff.size else 0.0, float(np.sqrt(np.mean(diff ** 2))) if diff.size else 0.0
+
+
+def assert_close(got, ref, dtype, what, o_bf16=None):
+    tol = TOL[dtype]
+    mx, rms = errors(got, ref)
+    if o_bf16:
+        floor = float(np.max(np.abs(torch.tensor(ref).to(torch.bfloat16).to(torch.float64).numpy() - ref))) if ref.size else 0.0
+        assert floor < tol["max"], f"{what}: tolerance unachievable at this seed (bf16 rounding floor {floor:.3g})"
+    assert mx <= tol["max"], f"{what}: max|err| {mx:.3g} > {tol['max']}"
+    if tol["rms"] is not None:
+        assert rms <= tol["rms"], f"{what}: rms {rms:.3g} > {tol['rms']}"
+    return mx, rms
+
+
+def assert_lse(got, ref, what):
+    mx = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    assert mx <= LSE_TOL, f"{what}: lse max|err| {mx:.3g} > {LSE_TOL}"
+    return mx

@@ -1,0 +1,93 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and rejects
+bad arguments before launching anything (no GPU needed for these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from io_aware_exact_15_amd import binding as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fa.lib()
+    names = _header_functions()
+    assert set(names) == set(fa.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_WORKSPACE, fa.FA_ERR_LAUNCH):
+        assert fa.fa_status_string(code).startswith("FA_")
+    assert fa.fa_status_string(12345) == "unknown fa_status"
+
+
+def _fwd(**kw):
+    a = dict(in_dtype=fa.FA_BF16, o_dtype=fa.FA_BF16, q=16, k=16, v=16, descale=None, o=16, lse=16,
+             B=1, H=1, N=8, d=64, scale=0.125, causal=0)
+    a.update(kw)
+    return fa.lib().fa_forward_typed(a["in_dtype"], a["o_dtype"], a["q"], a["k"], a["v"], a["descale"], a["o"],
+                                     a["lse"], a["B"], a["H"], a["N"], a["d"], ctypes.c_float(a["scale"]),
+                                     a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(q=18), fa.FA_ERR_INVALID_ARG),  # misaligned
+    (dict(in_dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(o_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),  # descale missing
+    (dict(in_dtype=fa.FA_FP8_E4M3, o_dtype=fa.FA_F32, descale=16), fa.FA_ERR_UNSUPPORTED),
+    (dict(descale=16), fa.FA_ERR_INVALID_ARG),  # descale given for bf16
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),  # empty batch: no-op
+    (dict(H=0), fa.FA_OK),
+    (dict(B=1 << 20, H=1 << 12, N=1 << 12), fa.FA_ERR_INVALID_ARG),  # grid overflow
+])
+def test_forward_validation(kw, status):
+    assert _fwd(**kw) == status
+
+
+def _bwd(ws_bytes=None, **kw):
+    a = dict(q=16, k=16, v=16, o=16, o_dtype=fa.FA_F32, do=16, lse=16, dq=16, dk=16, dv=16, ws=16,
+             B=1, H=2, N=40, d=128, scale=0.1, causal=1)
+    a.update(kw)
+    need = fa.fa_backward_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return fa.lib().fa_backward(a["q"], a["k"], a["v"], a["o"], a["o_dtype"], a["do"], a["lse"], a["dq"], a["dk"],
+                                a["dv"], a["ws"], ws_bytes, a["B"], a["H"], a["N"], a["d"], ctypes.c_float(a["scale"]),
+                                a["causal"], None)
+
+
+def test_workspace_size():
+    assert fa.fa_backward_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 64) == 256
+    assert fa.fa_backward_workspace_bytes(0, 1, 3, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=8), fa.FA_ERR_WORKSPACE),
+    (dict(B=0, q=None), fa.FA_OK),
+])
+def test_backward_validation(kw, status):
+    assert _bwd(**kw) == status
