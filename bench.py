@@ -1,0 +1,172 @@
+"""Throughput of the exact-attention hot path on one MI355X.
+
+Workload: causal attention, bf16 operands, B=1 H=32 N=16384 d=128, scale
+1/sqrt(d), synthetic N(0,1) inputs resident in HBM. One step is the whole
+path: the forward pass (saving O and lse) followed by the backward pass
+(D = rowsum(dO*O), dK/dV, dQ). Algorithmic FLOP: forward 4*B*H*N^2*d,
+backward 10*B*H*N^2*d, both halved for the causal mask.
+
+Prints one JSON line. Per-kernel durations come from HIP events recorded on
+the launch stream around every launch of the timed region.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = dict(name="fwd_bwd_bf16_causal_b1h32_n16384_d128", B=1, H=32, N=16384, d=128, causal=True, seed=3)
+
+
+def _flops(B, H, N, d, causal, kind):
+    f = {"fwd": 4, "bwd": 10}[kind] * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def cpu_baseline(w, rows_per_head=1536):
+    """The float64 oracle on host cores, on a bounded sample of the same workload.
+
+    Sample: `rows_per_head` seeded query rows of every head, each against all
+    keys (forward only). Value: the algorithmic causal FLOP of those rows
+    (4*d*(i+1) for row i) per second of oracle wall time.
+    """
+    import numpy as np
+
+    import oracle
+    from io_aware_exact_15_amd import inputs
+
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    inp = inputs.make_inputs(B, H, N, d, w["seed"], "bf16")
+    q, k, v = (inputs.to_numpy(inp[n]) for n in ("q", "k", "v"))
+    rows = inputs.sample_rows(w["seed"], B, H, N, rows_per_head)
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, 1.0 / math.sqrt(d), True, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = float(np.sum(4.0 * d * (rows + 1)))
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": f"forward, {rows_per_head} seeded query rows per head x {B * H} heads against all {N} keys, "
+                  f"float64 numpy ({dt:.2f} s wall, OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', 'unset')})",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs on a single "
+              "MI355X and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from io_aware_exact_15_amd import binding as fa
+    from io_aware_exact_15_amd import inputs
+
+    w = WORKLOAD
+    B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    inp = inputs.make_inputs(B, H, N, d, w["seed"], "bf16", with_do=True)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    o_bf = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev)
+    lse_bf = torch.empty_like(lse)
+    torch.cuda.synchronize()
+
+    # Backward availability (the step is forward-only until it is built).
+    have_bwd = True
+    dq = dk = dv = ws = None
+    try:
+        dq, dk, dv = (torch.empty(B, H, N, d, dtype=torch.float32, device=dev) for _ in range(3))
+        ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        fa.fa_forward_typed(fa.FA_BF16, fa.FA_F32, q, k, v, None, o, lse, scale, causal)
+        fa.fa_backward(q, k, v, o, fa.FA_F32, do, lse, dq, dk, dv, ws, scale, causal)
+    except fa.FAError as e:
+        if e.status != fa.FA_ERR_UNSUPPORTED:
+            raise
+        have_bwd = False
+    torch.cuda.synchronize()
+
+    def step(ev):
+        # headline forward: bf16 O
+        ev[0].record()
+        fa.fa_forward_typed(fa.FA_BF16, fa.FA_BF16, q, k, v, None, o_bf, lse_bf, scale, causal)
+        ev[1].record()
+        if have_bwd:
+            fa.fa_forward_typed(fa.FA_BF16, fa.FA_F32, q, k, v, None, o, lse, scale, causal)
+            ev[2].record()
+            fa.fa_backward(q, k, v, o, fa.FA_F32, do, lse, dq, dk, dv, ws, scale, causal)
+            ev[3].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_med = sorted(fwd_ms)[len(fwd_ms) // 2]
+    fwd_f = _flops(B, H, N, d, causal, "fwd")
+    fwd_tf = fwd_f / (fwd_med * 1e-3) / 1e12
+    res_fwd = {"ms_median": fwd_med, "ms_min": min(fwd_ms), "tflops": fwd_tf, "frac_of_bf16_peak": fwd_tf / PEAK_BF16_TFLOPS}
+    step_flops = fwd_f
+    if have_bwd:
+        fwd32_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        bwd_ms = [e[2].elapsed_time(e[3]) for e in evs]
+        bwd_med = sorted(bwd_ms)[len(bwd_ms) // 2]
+        bwd_f = _flops(B, H, N, d, causal, "bwd")
+        res_bwd = {"ms_median": bwd_med, "ms_min": min(bwd_ms), "tflops": bwd_f / (bwd_med * 1e-3) / 1e12}
+        fb_ms = sorted(a + b for a, b in zip(fwd32_ms, bwd_ms))[len(bwd_ms) // 2]
+        res_fb = {"ms_median": fb_ms, "tflops": (fwd_f + bwd_f) / (fb_ms * 1e-3) / 1e12}
+        step_flops = fwd_f + fwd_f + bwd_f
+    ms_per_step = wall / args.steps * 1e3
+
+    # Dominant kernel for the roofline object: the forward kernel (the only
+    # launch of the headline forward).
+    roofline = {"bound": "mfma", "kernel": "fwd_bf16_kernel", "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None}
+    out = {
+        "metric": "attention TFLOP/s (fwd, fwd+bwd) and % of MFMA peak, causal bf16 N=16K d=128",
+        "value": (res_fb["tflops"] if have_bwd else fwd_tf),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w["name"] if have_bwd else "fwd_bf16_causal_b1h32_n16384_d128",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal, "scale": scale,
+                   "value_is": "fwd+bwd TFLOP/s (fwd with fp32 O, then bwd)" if have_bwd else "fwd TFLOP/s (backward not built)"},
+        "fwd": res_fwd,
+        "roofline": roofline,
+    }
+    if have_bwd:
+        out["bwd"] = res_bwd
+        out["fwd_bwd"] = res_fb
+    out["step_flops"] = step_flops
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -121,13 +121,10 @@ __global__ __launch_bounds__(256, MINB) void fwd_bf16_kernel(
     for (int i = 0; i < CPT; ++i) {
       const int idx = tid + 256 * i, row = idx / (D / 8), c8 = idx % (D / 8);
       const int key = kb * BC + row;
-      if (key < N) {
-        kreg[i] = *(const i32x4*)(K + hoff + (size_t)key * D + c8 * 8);
-        vreg[i] = *(const i32x4*)(V + hoff + (size_t)key * D + c8 * 8);
-      } else {
-        kreg[i] = i32x4{};
-        vreg[i] = i32x4{};
-      }
+      const size_t off = hoff + (size_t)(key < N ? key : 0) * D + c8 * 8;  // clamped: always in bounds
+      const i32x4 a = *(const i32x4*)(K + off), b = *(const i32x4*)(V + off);
+      kreg[i] = key < N ? a : i32x4{};
+      vreg[i] = key < N ? b : i32x4{};
     }
   };
   auto store_lds = [&](int buf) {

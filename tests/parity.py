@@ -76,3 +76,27 @@ def assert_lse(got, ref, what):
     mx = float(np.max(np.abs(got - ref))) if got.size else 0.0
     assert mx <= LSE_TOL, f"{what}: lse max|err| {mx:.3g} > {LSE_TOL}"
     return mx
+
+
+def gpu_backward(inp, causal, o_dtype="f32", scale=None):
+    """Forward (saving O in o_dtype and lse) then fa_backward; returns CPU float64 (dq, dk, dv)."""
+    q = inp["q"]
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    odt = torch.float32 if o_dtype == "f32" else torch.bfloat16
+    o = torch.empty(B, H, N, d, dtype=odt, device=dev)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    fa.fa_forward_typed(fa.FA_BF16, FA_DT[o_dtype], qd, kd, vd, None, o, lse, scale, causal)
+    ws = torch.empty(max(fa.fa_backward_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8, device=dev)
+    dq, dk, dv = (torch.full((B, H, N, d), float("nan"), dtype=torch.float32, device=dev) for _ in range(3))
+    fa.fa_backward(qd, kd, vd, o, FA_DT[o_dtype], dod, lse, dq, dk, dv, ws, scale, causal)
+    torch.cuda.synchronize()
+    return tuple(t.cpu().to(torch.float64).numpy() for t in (dq, dk, dv))
+
+
+def oracle_backward(inp, causal, scale=None, heads=None):
+    d = inp["q"].shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    return oracle.backward(*(inputs.to_numpy(inp[n]) for n in ("q", "k", "v", "do")), scale, causal, heads=heads)

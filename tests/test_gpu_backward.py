@@ -1,0 +1,68 @@
+"""Backward parity: dQ, dK, dV from the HIP path (through the C ABI) vs the float64 oracle."""
+import numpy as np
+import pytest
+
+from io_aware_exact_15_amd import inputs
+from parity import assert_close, gpu_backward, oracle_backward
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(B, H, N, d, seed, causal, o_dtype="f32", heads=None):
+    print(f"case B={B} H={H} N={N} d={d} seed={seed} causal={causal} o={o_dtype} heads={heads}", flush=True)
+    inp = inputs.make_inputs(B, H, N, d, seed, "bf16", with_do=True)
+    got = gpu_backward(inp, causal, o_dtype)
+    ref = oracle_backward(inp, causal, heads=heads)
+    sel = (slice(None),) if heads is None else (tuple(b for b, _ in heads), tuple(h for _, h in heads))
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.all(np.isfinite(g)), name
+        mx, rms = assert_close(g[sel], r[sel], "bf16", name)
+        print(f"  {name}: max={mx:.3g} rms={rms:.3g}", flush=True)
+    return got, inp
+
+
+def test_workload_bwd_causal_b2h16_n4096_d128():
+    """B=2 H=16 N=4096 d=128 causal: every element of dQ, dK, dV of every head."""
+    w = inputs.WORKLOADS["bwd_bf16_causal_b2h16_n4096_d128"]
+    _check(w["B"], w["H"], w["N"], w["d"], w["seed"], True)
+
+
+EDGE = [
+    (1, 1, 1, 64), (1, 1, 1, 128), (1, 1, 17, 128), (1, 2, 63, 64), (2, 3, 100, 128), (1, 1, 129, 64),
+    (1, 8, 255, 128), (2, 8, 257, 64), (1, 3, 640, 128), (1, 16, 300, 64),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=[f"B{b}H{h}N{n}d{d}" for b, h, n, d in EDGE])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge(shape, causal):
+    B, H, N, d = shape
+    _check(B, H, N, d, 300 + N, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_saved_output(causal):
+    """The backward also accepts the bf16 O of the forward pass (D is then formed from it)."""
+    _check(1, 4, 500, 128, 21, causal, o_dtype="bf16")
+
+
+def test_noncausal_mid_size():
+    _check(1, 4, 2048, 128, 22, False)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_invariants(causal):
+    """Independent of the oracle: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per head."""
+    inp = inputs.make_inputs(1, 4, 1500, 128, 23, "bf16", with_do=True)
+    dq, dk, dv = gpu_backward(inp, causal)
+    do = inp["do"].double().numpy()
+    assert np.max(np.abs(dk.sum(axis=2))) <= 5e-2
+    assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 5e-2
+
+
+def test_deterministic():
+    inp = inputs.make_inputs(1, 8, 700, 128, 24, "bf16", with_do=True)
+    a = gpu_backward(inp, True)
+    b = gpu_backward(inp, True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
