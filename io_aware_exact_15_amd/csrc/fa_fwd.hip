@@ -379,7 +379,6 @@ static hipError_t launch_f32(const void* q, const void* k, const void* v, void* 
 int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
                    const float* descale, void* o, float* lse, int B, int H, int N, int d, float scale,
                    int causal, hipStream_t stream) {
-  (void)descale;
   const int BH = B * H;
   const float c = scale * kLog2e;
   hipError_t err;
@@ -389,6 +388,8 @@ int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, cons
   } else if (in_dtype == FA_F32) {
     err = (o_dtype == FA_BF16) ? FA_DISPATCH(launch_f32, d, causal, bf16, q, k, v, o, lse, BH, N, c, stream)
                                : FA_DISPATCH(launch_f32, d, causal, float, q, k, v, o, lse, BH, N, c, stream);
+  } else if (in_dtype == FA_FP8_E4M3 && o_dtype == FA_BF16) {
+    err = launch_forward_fp8(q, k, v, descale, o, lse, BH, N, d, scale, causal, stream);
   } else {
     return FA_ERR_UNSUPPORTED;
   }

@@ -11,6 +11,10 @@ int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, cons
                    const float* descale, void* o, float* lse, int B, int H, int N, int d,
                    float scale, int causal, hipStream_t stream);
 
+// FP8 E4M3 forward launch (descale: device pointer to {s_q, s_k, s_v}).
+hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const float* descale, void* o, float* lse,
+                              int BH, int N, int d, float scale, int causal, hipStream_t stream);
+
 // Backward launch; arguments already validated by the ABI layer.
 int launch_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                     const void* dO, const float* lse, float* dq, float* dk, float* dv,
