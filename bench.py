@@ -65,6 +65,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--counters", action="store_true",
+                    help="untimed: one float32 copy-kernel launch of known size (512 MiB read + 512 MiB written, "
+                         "the traffic calibration) and one step, for hardware-counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs on a single "
@@ -112,6 +115,17 @@ def main():
             ev[2].record()
             fa.fa_backward(q, k, v, o, fa.FA_F32, do, lse, dq, dk, dv, ws, scale, causal)
             ev[3].record()
+
+    if args.counters:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # copy kernel: reads 512 MiB, writes 512 MiB
+        torch.cuda.synchronize()
+        warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(warm)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "copy_bytes_each_way": src.numel() * 4}), flush=True)
+        return
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]

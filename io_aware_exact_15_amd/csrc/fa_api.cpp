@@ -20,6 +20,8 @@ int check_shape(int B, int H, int N, int d, float scale) {
   // grid = B*H*ceil(N/32) must fit in an int; element offsets use size_t.
   const long long bh = (long long)B * H;
   if (bh > 0 && bh * ((N + 31) / 32) > INT_MAX) return FA_ERR_INVALID_ARG;
+  // One head of K or V must be addressable by a 32-bit buffer offset.
+  if ((long long)N * d * 4 > 0xffffffffLL) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

@@ -73,4 +73,45 @@ __device__ __forceinline__ bf16x8 cat4(s16x4 lo, s16x4 hi) {
 // Value held by the partner lane in the other half-wave (lane ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of x over the lane pair (l, l ^ 32) with one v_permlane32_swap:
+// the swap returns {lower half of x in both halves, upper half of x in both
+// halves}, so combining the two results gives the pair value in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Buffer resource (V#) over [base, base + bytes) as four SGPR words: 48-bit
+// base, stride 0, num_records = bytes, default format word. Buffer loads at
+// offsets past `bytes` return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  return i32x4{(int)(unsigned)b, (int)((unsigned)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// LDS address (byte offset inside the workgroup's LDS) of a __shared__ pointer.
+__device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(size_t)(const FA_LDS void*)p; }
+
+// 16 bytes per lane from buffer byte offset `voff` straight into LDS (LDS DMA):
+// lane l's data lands at lds_base + 16 * l; lds_base must be wave-uniform.
+// Issued as inline asm so that the compiler does not make every later LDS
+// read wait for it: the caller owns the ordering (wait_vmem() then a
+// workgroup barrier before the destination is read, and no DMA into a
+// buffer that another wave may still be reading). M0 is set here and is not
+// relied upon by compiler-generated code in these kernels.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds_base, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace fa

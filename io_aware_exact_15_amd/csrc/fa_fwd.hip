@@ -62,190 +62,207 @@ template <> struct OutStore<float> {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 operands. D: head size; QT: 32-row query tiles per wave; BC: keys per
-// block; 4 waves per workgroup (BR = 128 * QT query rows).
-template <int D, int QT, int BC, bool CAUSAL, typename OutT, int MINB>
-__global__ __launch_bounds__(256, MINB) void fwd_bf16_kernel(
+// bf16 operands. 8 waves x 32 query rows (BR = 256) per workgroup, blocks of
+// 64 keys. Two waves share each SIMD, so one wave's softmax overlaps the
+// other's matrix-core work.
+//
+// K/V tiles go HBM -> LDS with buffer loads that write LDS directly (no
+// staging registers; rows past N come back as zeros) into a 2-stage ring.
+// Tiles are row-major, D*2 bytes per row, with the 16-byte chunks of row r
+// XOR-permuted by swz(r) so that both the row reads of K (ds_read_b128, 16
+// rows at one column) and the transposing reads of V (ds_read_b64_tr_b16, 4
+// rows x 64 bytes) hit distinct LDS banks.
+//
+// Lazy rescaling: the running max m that the exponentials subtract is only
+// moved when a block's max exceeds it by more than kTau (log2 units). Until
+// then p = exp2(s*c - m) may reach 2^kTau, which bf16 and the float32
+// accumulators hold without loss, and since l and the accumulator share the
+// same m the final O = acc / l is unchanged. For typical data the max is
+// settled by the first block, and the per-block rescale of the 64 accumulator
+// registers disappears.
+constexpr float kTau = 8.f;
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return (4 * (r & 3)) ^ ((r >> 2) & 3);  // 16 chunks per row
+  return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);        // 8 chunks per row
+}
+
+template <int D, bool CAUSAL, typename OutT>
+__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float c) {
-  constexpr int BR = 128 * QT;
-  constexpr int KS = D + 8;    // K tile row stride (elements), 16-byte multiple
-  constexpr int VS = D + 16;   // V tile row stride
-  constexpr int KT = BC * KS, VT = BC * VS;
-  constexpr int NKT = BC / 32;  // 32-key sub-tiles per block
-  constexpr int NDT = D / 32;   // 32-dim output tiles
-  constexpr int NKS = D / 16;   // k-steps of S^T = K Q^T
-  constexpr int CHUNKS = BC * D / 8;  // 16-byte chunks per K (or V) tile
-  constexpr int CPT = CHUNKS / 256;
-  static_assert(CHUNKS % 256 == 0, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (KT + VT)];
+  constexpr int NW = 8, BR = 32 * NW, BC = 64;
+  constexpr int ROWB = 2 * D;          // bytes per tile row
+  constexpr int TILEB = BC * ROWB;     // bytes per K (or V) tile
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int NI = CPR / NW;         // load instructions per wave per tile
+  constexpr int NDT = D / 32, NKS = D / 16;
+  static_assert(NI >= 1 && CPR % NW == 0, "tile load split");
+  __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
 
   int bh, qb;
   map_block(blockIdx.x, BH, nqb, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
   const size_t hoff = (size_t)bh * N * D;
-  const int q0 = qb * BR + wave * 32 * QT;  // first query row of this wave
+  const int qw = qb * BR + 32 * wave;  // first query row of this wave
+  const int q = qw + col;
+
+  const i32x4 kr = make_rsrc(K + hoff, (unsigned)N * ROWB);
+  const i32x4 vr = make_rsrc(V + hoff, (unsigned)N * ROWB);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // Load addressing: instruction n of this wave fills tile chunks
+  // 64 (NI wave + n) + lane, i.e. row p / CPR, physical chunk p % CPR, which
+  // holds logical chunk (p % CPR) ^ swz(row).
+  unsigned goff[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int p = 64 * (NI * wave + n) + lane, row = p / CPR, pc = p % CPR;
+    goff[n] = row * ROWB + 16 * (pc ^ swz<D>(row));
+  }
+  auto issue_loads = [&](int kb, char* st) {
+    const unsigned base = (unsigned)kb * TILEB;
+    const unsigned la = lds_addr(st) + 1024u * NI * wave_u;
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      load_lds16(kr, la + 1024u * n, base + goff[n]);
+      load_lds16(vr, la + TILEB + 1024u * n, base + goff[n]);
+    }
+  };
+
+  // Read addressing (byte offsets inside a tile).
+  int koff[NKS];  // K row (32 kt + col), logical chunk 2 kk + hi; + kt * 32 * ROWB
+#pragma unroll
+  for (int kk = 0; kk < NKS; ++kk) koff[kk] = col * ROWB + 16 * ((2 * kk + hi) ^ swz<D>(col));
+  int voff[NDT][2];  // V row 4 hi + (j >> 2) + 8 sec, byte column 64 dt + 32 g + 8 (j & 3)
+  {
+    const int j = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int r = 4 * hi + (j >> 2) + 8 * sec;
+        const int bcol = 64 * dt + 32 * g + 8 * (j & 3);
+        voff[dt][sec] = r * ROWB + 16 * ((bcol >> 4) ^ swz<D>(r)) + (bcol & 15);
+      }
+  }
 
   // Q^T fragments (B operand): lane holds Q[q][16 ks + 8 hi + 0..7].
-  bf16x8 qf[QT][NKS];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int q = q0 + 32 * qt + col;
+  bf16x8 qf[NKS];
+  {
     const bf16x8* src = (const bf16x8*)(Q + hoff + (size_t)(q < N ? q : 0) * D);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 x = src[2 * ks + hi];
-      if (q >= N) x = bf16x8{};
-      qf[qt][ks] = x;
+      const bf16x8 x = src[2 * ks + hi];
+      qf[ks] = q < N ? x : bf16x8{};
     }
   }
 
-  f32x16 acc[QT][NDT];
-  float m[QT], l[QT];
+  f32x16 acc[NDT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m[qt] = kNegInf;
-    l[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x16{};
-  }
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+  float m = kNegInf, l = 0.f;
 
   const int nkb_all = (N + BC - 1) / BC;
   const int q_last = min(N - 1, qb * BR + BR - 1);
   const int nkb = CAUSAL ? min(nkb_all, q_last / BC + 1) : nkb_all;
 
-  i32x4 kreg[CPT], vreg[CPT];
-  auto load_regs = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i, row = idx / (D / 8), c8 = idx % (D / 8);
-      const int key = kb * BC + row;
-      const size_t off = hoff + (size_t)(key < N ? key : 0) * D + c8 * 8;  // clamped: always in bounds
-      const i32x4 a = *(const i32x4*)(K + off), b = *(const i32x4*)(V + off);
-      kreg[i] = key < N ? a : i32x4{};
-      vreg[i] = key < N ? b : i32x4{};
-    }
-  };
-  auto store_lds = [&](int buf) {
-    bf16* ks = smem + buf * (KT + VT);
-    bf16* vs = ks + KT;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i, row = idx / (D / 8), c8 = idx % (D / 8);
-      *(i32x4*)(ks + row * KS + c8 * 8) = kreg[i];
-      *(i32x4*)(vs + row * VS + c8 * 8) = vreg[i];
-    }
-  };
-
-  load_regs(0);
-  store_lds(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load_regs(kb + 1);
-    const bf16* ks = smem + buf * (KT + VT);
-    const bf16* vs = ks + KT;
+  auto compute = [&](int kb, const char* st) {
     const int k0 = kb * BC;
-    const bool active = !CAUSAL || k0 <= q0 + 32 * QT - 1;
-    if (active) {
-      // S^T = K Q^T for BC keys x 32 QT queries.
-      f32x16 s[QT][NKT];
+    if (CAUSAL && k0 > qw + 31) return;  // every key of the block is after every query of the wave
+    const char* ks = st;
+    const char* vs = st + TILEB;
+    f32x16 s[2];
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
+      bf16x8 a[NKS];
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = f32x16{};
+      for (int kk = 0; kk < NKS; ++kk) a[kk] = *(const bf16x8*)(ks + koff[kk] + kt * 32 * ROWB);
+      s[kt] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(ks + (32 * kt + col) * KS + 16 * kk + 8 * hi);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma_bf16(a, qf[qt][kk], s[qt][kt]);
-        }
-      }
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-      bf16x8 pf[QT][NKT][2];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if (need_mask) {
-          const int q = q0 + 32 * qt + col;
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 32 * kt + 8 * (i / 4) + 4 * hi + (i % 4);
-              if (key >= N || (CAUSAL && key > q)) s[qt][kt][i] = kNegInf;
-            }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qt][kt][i]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m[qt], mx * c);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m[qt] - m_use);
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(__builtin_fmaf(s[qt][kt][i], c, -m_use));
-            s[qt][kt][i] = p;
-            rs += p;
-          }
-        rs += xor32(rs);
-        l[qt] = l[qt] * alpha + rs;
-        m[qt] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            bf16x8 x;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = (bf16)s[qt][kt][8 * h2 + j];
-            pf[qt][kt][h2] = x;
-          }
-      }
-      // O^T += V^T P^T. Contraction slot order per 16-key step (matching the
-      // accumulator rows a lane holds): lanes 0-31 keys {0-3, 8-11}, lanes
-      // 32-63 keys {4-7, 12-15}.
-      const int trow = 4 * hi + ((lane & 15) >> 2);
-      const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const bf16* p0 = vs + (32 * kt + 16 * h2 + trow) * VS + 32 * dt + tcol;
-            const bf16x8 a = cat4(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * VS));
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma_bf16(a, pf[qt][kt][h2], acc[qt][dt]);
-          }
+      for (int kk = 0; kk < NKS; ++kk) s[kt] = mfma_bf16(a[kk], qf[kk], s[kt]);
     }
-    if (kb + 1 < nkb) store_lds(buf ^ 1);
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
+      // key index of register i of tile kt: k0 + 32 kt + 8 (i / 4) + 4 hi + i % 4
+      const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 4 * hi;  // keep iff offset <= lim
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kt + 8 * (i / 4) + (i % 4) > lim) s[kt][i] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
+    mx = pair_max(mx) * c;
+    const bool upd = mx > m + kTau;
+    if (__builtin_amdgcn_ballot_w64(upd)) {  // wave-uniform, rare after the first block
+      const float alpha = upd ? fast_exp2(m - mx) : 1.f;
+      if (upd) m = mx;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    }
+    const float nm = (m == kNegInf) ? 0.f : -m;
+    float rs0 = 0.f, rs1 = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(s[kt][8 * h2 + j], c, nm));
+        rs0 += (p[0] + p[1]) + (p[2] + p[3]);
+        rs1 += (p[4] + p[5]) + (p[6] + p[7]);
+        pf[kt][h2] = bf16x8{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3],
+                            (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+      }
+    l += pair_sum(rs0 + rs1);
+    // O^T += V^T P^T; contraction slots per 16-key step: lanes 0-31 keys
+    // {0-3, 8-11}, lanes 32-63 keys {4-7, 12-15} (the accumulator rows).
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int rb = (32 * kt + 16 * h2) * ROWB;
+          const bf16x8 a = cat4(lds_read_tr16((const bf16*)(vs + voff[dt][0] + rb)),
+                                lds_read_tr16((const bf16*)(vs + voff[dt][1] + rb)));
+          acc[dt] = mfma_bf16(a, pf[kt][h2], acc[dt]);
+        }
+  };
+
+  issue_loads(0, lds[0]);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    wait_vmem();
     __syncthreads();
+    if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
+    compute(kb, lds[0]);
+    if (kb + 1 < nkb) {
+      wait_vmem();
+      __syncthreads();
+      if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
+      compute(kb + 1, lds[1]);
+    }
   }
 
-  // Epilogue: O = acc / l, lse = (m + log2 l) * ln 2 (m is in log2 units of the scaled scores).
+  // Epilogue: O = acc / l, lse = (m + log2 l) * ln 2 (m in log2 units of the scaled scores).
+  if (q < N) {
+    const float inv = 1.f / l;
+    OutT* dst = O + hoff + (size_t)q * D + 4 * hi;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int q = q0 + 32 * qt + col;
-    if (q < N) {
-      const float inv = 1.f / l[qt];
-      OutT* dst = O + hoff + (size_t)q * D + 4 * hi;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          OutStore<OutT>::store4(dst + 32 * dt + 8 * g, acc[qt][dt][4 * g] * inv, acc[qt][dt][4 * g + 1] * inv,
-                                 acc[qt][dt][4 * g + 2] * inv, acc[qt][dt][4 * g + 3] * inv);
-      if (hi == 0) LSE[(size_t)bh * N + q] = (m[qt] + __log2f(l[qt])) * kLn2;
-    }
+      for (int g = 0; g < 4; ++g)
+        OutStore<OutT>::store4(dst + 32 * dt + 8 * g, acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
+                               acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+    if (hi == 0) LSE[(size_t)bh * N + q] = (m + __log2f(l)) * kLn2;
   }
 }
 
@@ -356,10 +373,9 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
 template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                               int N, float c, hipStream_t st) {
-  constexpr int QT = 1, BC = 64;
-  const int nqb = (N + 128 * QT - 1) / (128 * QT);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, BC, CAUSAL, OutT, 2>), dim3(BH * nqb), dim3(256), 0, st,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, N, nqb, c);
+  const int nqb = (N + 255) / 256;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OutT>), dim3(BH * nqb), dim3(512), 0, st, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, N, nqb, c);
   return hipGetLastError();
 }
 

@@ -59,6 +59,7 @@ def _fwd(**kw):
     (dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),  # empty batch: no-op
     (dict(H=0), fa.FA_OK),
     (dict(B=1 << 20, H=1 << 12, N=1 << 12), fa.FA_ERR_INVALID_ARG),  # grid overflow
+    (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),  # head larger than a 32-bit buffer range
 ])
 def test_forward_validation(kw, status):
     assert _fwd(**kw) == status
