@@ -114,4 +114,11 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds_base, unsign
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace fa

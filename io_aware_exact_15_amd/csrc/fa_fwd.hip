@@ -63,7 +63,7 @@ template <> struct OutStore<float> {
 
 // ---------------------------------------------------------------------------
 // bf16 operands. 8 waves x 32 query rows (BR = 256) per workgroup, blocks of
-// 64 keys. Two waves share each SIMD, so one wave's softmax overlaps the
+// BC keys (128 for the workloads here). Two waves share each SIMD, so one wave's softmax overlaps the
 // other's matrix-core work.
 //
 // K/V tiles go HBM -> LDS with buffer loads that write LDS directly (no
@@ -88,15 +88,16 @@ __device__ __forceinline__ int swz(int r) {
   return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);        // 8 chunks per row
 }
 
-template <int D, bool CAUSAL, typename OutT>
+template <int D, int BC, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float c) {
-  constexpr int NW = 8, BR = 32 * NW, BC = 64;
+  constexpr int NW = 8, BR = 32 * NW;
+  constexpr int NKT = BC / 32;  // 32-key tiles per block
   constexpr int ROWB = 2 * D;          // bytes per tile row
   constexpr int TILEB = BC * ROWB;     // bytes per K (or V) tile
   constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int NI = CPR / NW;         // load instructions per wave per tile
+  constexpr int NI = CPR * BC / 64 / NW;  // load instructions per wave per tile
   constexpr int NDT = D / 32, NKS = D / 16;
   static_assert(NI >= 1 && CPR % NW == 0, "tile load split");
   __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   unsigned goff[NI];
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
-    const int p = 64 * (NI * wave + n) + lane, row = p / CPR, pc = p % CPR;
+    const int p = 64 * (NI * wave + n) + lane, row = p / CPR, pc = p % CPR;  // row < BC
     goff[n] = row * ROWB + 16 * (pc ^ swz<D>(row));
   }
   auto issue_loads = [&](int kb, char* st) {
@@ -174,9 +175,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     if (CAUSAL && k0 > qw + 31) return;  // every key of the block is after every query of the wave
     const char* ks = st;
     const char* vs = st + TILEB;
-    f32x16 s[2];
+    f32x16 s[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < NKT; ++kt) {
       bf16x8 a[NKS];
 #pragma unroll
       for (int kk = 0; kk < NKS; ++kk) a[kk] = *(const bf16x8*)(ks + koff[kk] + kt * 32 * ROWB);
@@ -188,17 +189,20 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
       // key index of register i of tile kt: k0 + 32 kt + 8 (i / 4) + 4 hi + i % 4
       const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 4 * hi;  // keep iff offset <= lim
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * kt + 8 * (i / 4) + (i % 4) > lim) s[kt][i] = kNegInf;
     }
-    float mx = kNegInf;
+    float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; kt += 2)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
-    mx = pair_max(mx) * c;
+      for (int i = 0; i < 16; i += 2) {
+        mx0 = fmaxf(fmaxf(mx0, s[kt][i]), s[kt][i + 1]);
+        mx1 = fmaxf(fmaxf(mx1, s[kt + 1][i]), s[kt + 1][i + 1]);
+      }
+    const float mx = pair_max(fmaxf(mx0, mx1)) * c;
     const bool upd = mx > m + kTau;
     if (__builtin_amdgcn_ballot_w64(upd)) {  // wave-uniform, rare after the first block
       const float alpha = upd ? fast_exp2(m - mx) : 1.f;
@@ -209,9 +213,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     }
     const float nm = (m == kNegInf) ? 0.f : -m;
     float rs0 = 0.f, rs1 = 0.f;
-    bf16x8 pf[2][2];
+    bf16x8 pf[NKT][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         float p[8];
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int rb = (32 * kt + 16 * h2) * ROWB;
@@ -374,7 +378,7 @@ template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                               int N, float c, hipStream_t st) {
   const int nqb = (N + 255) / 256;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OutT>), dim3(BH * nqb), dim3(512), 0, st, (const bf16*)q,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, 128, CAUSAL, OutT>), dim3(BH * nqb), dim3(512), 0, st, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, N, nqb, c);
   return hipGetLastError();
 }
