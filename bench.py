@@ -31,6 +31,42 @@ def _flops(B, H, N, d, causal, kind):
     return f / 2 if causal else f
 
 
+def _source_sha(names):
+    """sha256 over the kernel sources a measurement depends on."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "io_aware_exact_15_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.hpp"], "bwd": ["fa_bwd.hip", "fa_device.hpp"]}
+TRAFFIC_FILES = {"fwd": "fwd_bf16_causal_b1h32_n16384_d128_traffic.md",
+                 "bwd": "bwd_bf16_causal_b1h32_n16384_d128_traffic.md"}
+
+
+def _recorded_traffic(kind):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    (profiles/), or None when absent or taken on a different kernel source."""
+    import re
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILES[kind])
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(2) != _source_sha(KERNEL_SOURCES[kind]):
+        return None
+    return int(m.group(1))
+
+
+def _roofline(kernel, kind, flops, mean_ms):
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _recorded_traffic(kind),
+            "algorithmic_flop_per_launch": flops, "mean_launch_ms": mean_ms}
+
+
 def cpu_baseline(w, rows_per_head=1536):
     """The float64 oracle on host cores, on a bounded sample of the same workload.
 
@@ -140,25 +176,29 @@ def main():
 
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     fwd_med = sorted(fwd_ms)[len(fwd_ms) // 2]
+    fwd_mean = sum(fwd_ms) / len(fwd_ms)
     fwd_f = _flops(B, H, N, d, causal, "fwd")
     fwd_tf = fwd_f / (fwd_med * 1e-3) / 1e12
-    res_fwd = {"ms_median": fwd_med, "ms_min": min(fwd_ms), "tflops": fwd_tf, "frac_of_bf16_peak": fwd_tf / PEAK_BF16_TFLOPS}
+    res_fwd = {"ms_median": fwd_med, "ms_mean": fwd_mean, "ms_min": min(fwd_ms), "tflops": fwd_tf,
+               "frac_of_bf16_peak": fwd_tf / PEAK_BF16_TFLOPS}
+    roof_fwd = _roofline("fwd_bf16_kernel (bf16 O)", "fwd", fwd_f, fwd_mean)
     step_flops = fwd_f
+    roofline = roof_fwd
     if have_bwd:
         fwd32_ms = [e[1].elapsed_time(e[2]) for e in evs]
         bwd_ms = [e[2].elapsed_time(e[3]) for e in evs]
         bwd_med = sorted(bwd_ms)[len(bwd_ms) // 2]
+        bwd_mean = sum(bwd_ms) / len(bwd_ms)
         bwd_f = _flops(B, H, N, d, causal, "bwd")
-        res_bwd = {"ms_median": bwd_med, "ms_min": min(bwd_ms), "tflops": bwd_f / (bwd_med * 1e-3) / 1e12}
+        res_bwd = {"ms_median": bwd_med, "ms_mean": bwd_mean, "ms_min": min(bwd_ms),
+                   "tflops": bwd_f / (bwd_med * 1e-3) / 1e12}
         fb_ms = sorted(a + b for a, b in zip(fwd32_ms, bwd_ms))[len(bwd_ms) // 2]
         res_fb = {"ms_median": fb_ms, "tflops": (fwd_f + bwd_f) / (fb_ms * 1e-3) / 1e12}
         step_flops = fwd_f + fwd_f + bwd_f
+        if bwd_mean > fwd_mean:  # the backward pass dominates the step
+            roofline = _roofline("fa_backward (bwd_pre + bwd_dkdv + bwd_dq)", "bwd", bwd_f, bwd_mean)
     ms_per_step = wall / args.steps * 1e3
 
-    # Dominant kernel for the roofline object: the forward kernel (the only
-    # launch of the headline forward).
-    roofline = {"bound": "mfma", "kernel": "fwd_bf16_kernel", "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None}
     out = {
         "metric": "attention TFLOP/s (fwd, fwd+bwd) and % of MFMA peak, causal bf16 N=16K d=128",
         "value": (res_fb["tflops"] if have_bwd else fwd_tf),
@@ -172,6 +212,7 @@ def main():
                    "value_is": "fwd+bwd TFLOP/s (fwd with fp32 O, then bwd)" if have_bwd else "fwd TFLOP/s (backward not built)"},
         "fwd": res_fwd,
         "roofline": roofline,
+        "roofline_fwd": roof_fwd,
     }
     if have_bwd:
         out["bwd"] = res_bwd
