@@ -88,7 +88,10 @@ int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, co
 
 /*
  * fa_backward_workspace_bytes -- device workspace that fa_backward needs:
- * one float32 per row (D_i = sum_t dO_it O_it), rounded up to 256 bytes.
+ * two float32 per row (D_i = sum_t dO_it O_it and -lse_i*log2(e)) and fp16
+ * copies of Q, K, V and dO (the matrix-core operands of the backward pass),
+ * each region rounded up to 256 bytes. 0 for an empty batch or an
+ * unsupported head size.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 
@@ -100,9 +103,13 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
  *                 D = rowsum(dO * O) is formed from it).
  *   lse         : float32 [B,H,N] from the same forward call.
  *   dq, dk, dv  : float32 [B,H,N,d] outputs, fully overwritten.
- *   workspace   : device buffer of at least fa_backward_workspace_bytes().
+ *   workspace   : device buffer of at least fa_backward_workspace_bytes();
+ *                 its contents on entry are ignored and on return unspecified.
  * The probabilities are recomputed block by block from Q, K and lse; no
- * N x N buffer exists at any time.
+ * N x N buffer exists at any time. The matrix-core operands are fp16: bf16
+ * inputs are converted exactly while |x| lies in [2^-14, 65504]; smaller
+ * magnitudes keep fp16's subnormal resolution (2^-24) and larger ones are
+ * outside the supported range.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                 const void* dO, const float* lse, float* dq, float* dk, float* dv,

@@ -66,10 +66,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
-  (void)d;
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
-  const size_t bytes = (size_t)B * H * N * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  return fa::backward_workspace_bytes((size_t)B * H * N, d);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
@@ -85,8 +83,8 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, int 
     return FA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d) || !aligned16(workspace))
     return FA_ERR_WORKSPACE;
-  return fa::launch_backward(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, (float*)workspace, B, H, N, d, scale,
-                             causal, (hipStream_t)stream);
+  return fa::launch_backward(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal,
+                             (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -15,10 +15,15 @@ int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, cons
 hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const float* descale, void* o, float* lse,
                               int BH, int N, int d, float scale, int causal, hipStream_t stream);
 
-// Backward launch; arguments already validated by the ABI layer.
+// Backward launch; arguments already validated by the ABI layer. `workspace`
+// holds at least backward_workspace_bytes(B*H*N, d) bytes.
 int launch_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                     const void* dO, const float* lse, float* dq, float* dk, float* dv,
-                    float* delta, int B, int H, int N, int d, float scale, int causal,
+                    void* workspace, int B, int H, int N, int d, float scale, int causal,
                     hipStream_t stream);
+
+// Backward workspace: D and -lse*log2(e) (float32 per row) and fp16 copies of
+// Q, K, V, dO, each region 256-byte aligned.
+size_t backward_workspace_bytes(size_t rows, int d);
 
 }  // namespace fa

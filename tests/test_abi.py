@@ -77,9 +77,12 @@ def _bwd(ws_bytes=None, **kw):
 
 
 def test_workspace_size():
-    assert fa.fa_backward_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
-    assert fa.fa_backward_workspace_bytes(1, 1, 3, 64) == 256
+    rows = 2 * 16 * 4096
+    assert fa.fa_backward_workspace_bytes(2, 16, 4096, 128) == 2 * rows * 4 + 4 * rows * 128 * 2
+    # each of the six regions rounds up to 256 bytes
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 64) == 2 * 256 + 4 * 512
     assert fa.fa_backward_workspace_bytes(0, 1, 3, 64) == 0
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 96) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
