@@ -33,6 +33,8 @@
 // LDS tiles use the forward pass's XOR swizzle (16-byte chunk c of row r at
 // c ^ swz(r)), which keeps both row reads (ds_read_b128) and transposing reads
 // (ds_read_b64_tr_b16) free of bank conflicts.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 #include "../../include/fa.h"
@@ -150,38 +152,54 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV. 4 waves x 32 keys (BKV = 128); query blocks of BQ = 64 rows.
+// dK, dV. 8 waves per workgroup of 128 keys: wave w owns key group w % 4
+// (32 keys) and query half w / 4 of every 64-row query block, so two waves
+// share each SIMD and each key group, and each keeps only its own partial
+// dK, dV accumulators (128 registers). K stays in registers as the B
+// operand of S = Q K^T; the workgroup's V tile stays resident in LDS and is
+// read as the B operand of dP = dO V^T. The two partial sums of a key group
+// are added through LDS at the end.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdWs ws, float* __restrict__ dK, float* __restrict__ dV,
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __restrict__ dK, float* __restrict__ dV,
                                                           int BH, int N, int nkb, float c, float scale) {
-  constexpr int NW = 4, BKV = 32 * NW, BQ = 64;
+  constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int ROWB = 2 * D, TILEB = BQ * ROWB, CPR = D / 8;
-  constexpr int NPW = CPR * BQ / 64 / NW;  // 1024-byte DMA instructions per wave per tile
+  constexpr int VTB = BKV * ROWB;           // resident K (and V) tile bytes
+  constexpr int NPW = CPR * BQ / 64 / NW;   // 1024-byte DMA instructions per wave per Q (or dO) tile
+  constexpr int NPV = CPR * BKV / 64 / NW;  // ... per wave for the V tile
   constexpr int NKS = D / 16, NDT = D / 32;
-  constexpr int NST = 3;
+  constexpr int NST = 2;
   constexpr int STB = 2 * TILEB + 2 * BQ * 4;  // Q tile, dO tile, NL[BQ], D[BQ]
-  static_assert(NPW >= 1, "tile split");
+  static_assert(NPW >= 1 && NPV >= 1, "tile split");
+  static_assert(NST * STB >= 4 * 32 * D * 4 * 2 / 2, "reduction buffer fits in the ring");
+  __shared__ __attribute__((aligned(1024))) char lds_k[VTB];
+  __shared__ __attribute__((aligned(1024))) char lds_v[VTB];
   __shared__ __attribute__((aligned(1024))) char lds[NST][STB];
 
   int bh, kb;
   map_block_b(blockIdx.x, BH, nkb, CAUSAL, bh, kb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
+  const int kg = wave & 3, qh = wave >> 2;  // key group, query half
   const size_t hoff = (size_t)bh * N * D;
-  const int k0w = kb * BKV + 32 * wave;  // first key of this wave
+  const int k0w = kb * BKV + 32 * kg;  // first key of this wave
   const int key = k0w + col;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   const i32x4 qr = make_rsrc(ws.q + hoff, (unsigned)N * ROWB);
   const i32x4 orr = make_rsrc(ws.dO + hoff, (unsigned)N * ROWB);
+  const i32x4 vr = make_rsrc(ws.v + hoff, (unsigned)N * ROWB);
+  const i32x4 kr = make_rsrc(ws.k + hoff, (unsigned)N * ROWB);
   const i32x4 nlr = make_rsrc(ws.NL + (size_t)bh * N, (unsigned)N * 4);
   const i32x4 dr = make_rsrc(ws.Dv + (size_t)bh * N, (unsigned)N * 4);
+  // DMA addressing: instruction n of this wave fills tile chunks 64 (NP wave + n) + lane.
+  auto dma_off = [&](int n_global) {
+    const int p = 64 * n_global + lane, row = p / CPR, pc = p % CPR;
+    return (unsigned)(row * ROWB + 16 * (pc ^ swz_b<D>(row)));
+  };
   unsigned goff[NPW];
 #pragma unroll
-  for (int n = 0; n < NPW; ++n) {
-    const int p = 64 * (NPW * wave + n) + lane, row = p / CPR, pc = p % CPR;
-    goff[n] = row * ROWB + 16 * (pc ^ swz_b<D>(row));
-  }
+  for (int n = 0; n < NPW; ++n) goff[n] = dma_off(NPW * wave + n);
   // Waves 0 and 1 also bring the block's 64 NL and 64 D values (4 bytes per lane).
   const bool row_loader = wave_u < 2;
   auto issue_loads = [&](int qb, int st) {
@@ -202,21 +220,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
     }
   };
 
-  // K, V as B operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
-  f16x8 kf[NKS], vf[NKS];
+  // K and V tiles of the workgroup, once (rows past N read as zeros).
   {
-    const int kr = key < N ? key : 0;
-    const f16x8* ksrc = (const f16x8*)(ws.k + hoff + (size_t)kr * D);
-    const f16x8* vsrc = (const f16x8*)(ws.v + hoff + (size_t)kr * D);
+    const unsigned base = (unsigned)kb * VTB;
+    const unsigned lk = lds_addr(lds_k) + 1024u * NPV * wave_u;
+    const unsigned lv = lds_addr(lds_v) + 1024u * NPV * wave_u;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const f16x8 a = ksrc[2 * ks + hi], b = vsrc[2 * ks + hi];
-      kf[ks] = key < N ? a : f16x8{};
-      vf[ks] = key < N ? b : f16x8{};
+    for (int n = 0; n < NPV; ++n) {
+      const unsigned off = base + dma_off(NPV * wave + n);
+      load_lds16(kr, lk + 1024u * n, off);
+      load_lds16(vr, lv + 1024u * n, off);
     }
   }
-  // Read offsets: rows 32 qt + col at logical chunk 2 kk + hi (A operands);
-  // transposing reads at row 4 hi + (j >> 2) + 8 sec, byte column 64 dt + 32 g + 8 (j & 3).
+  // Row reads at row r, logical chunk 2 kk + hi; transposing reads at row
+  // 4 hi + (j >> 2) + 8 sec, byte column 64 dt + 32 g + 8 (j & 3).
   int roff[NKS];
 #pragma unroll
   for (int kk = 0; kk < NKS; ++kk) roff[kk] = col * ROWB + 16 * ((2 * kk + hi) ^ swz_b<D>(col));
@@ -232,6 +249,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
         toff[dt][sec] = r * ROWB + 16 * ((bcol >> 4) ^ swz_b<D>(r)) + (bcol & 15);
       }
   }
+  const char* krow = lds_k + 32 * kg * ROWB;  // this wave's 32 K rows (B operand of S)
+  const char* vrow = lds_v + 32 * kg * ROWB;  // this wave's 32 V rows (B operand of dP)
 
   f32x16 dk[NDT], dv[NDT];
 #pragma unroll
@@ -239,30 +258,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
 
   const int nqb = (N + BQ - 1) / BQ;
   const int qb0 = CAUSAL ? (kb * BKV) / BQ : 0;
-  // With 128 keys per workgroup and 64-row query blocks, only the first two
-  // query blocks can hold a query before some key of the workgroup.
   const int qb_unmasked = CAUSAL ? qb0 + BKV / BQ : 0;
 
-  // One 32-query tile: S, dP -> P, dS -> dV, dK.
-  auto tile = [&](const char* st, int qt, int q0, bool masked) {
-    const char* qs = st;
-    const char* os = st + TILEB;
-    const float* nl = (const float*)(st + 2 * TILEB);
+  // This wave's 32-query tile of the block in stage st: S, dP -> P, dS -> dV, dK.
+  auto tile = [&](const char* st, int q0, auto masked_c) {
+    constexpr bool masked = decltype(masked_c)::value;
+    const char* qs = st + 32 * qh * ROWB;
+    const char* os = st + TILEB + 32 * qh * ROWB;
+    const float* nl = (const float*)(st + 2 * TILEB) + 32 * qh;
     const float* dd = nl + BQ;
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      const f16x8 aq = *(const f16x8*)(qs + 32 * qt * ROWB + roff[kk]);
-      const f16x8 ao = *(const f16x8*)(os + 32 * qt * ROWB + roff[kk]);
-      s = mfma_f16(aq, kf[kk], s);
-      dp = mfma_f16(ao, vf[kk], dp);
+      const f16x8 aq = *(const f16x8*)(qs + roff[kk]);
+      const f16x8 ao = *(const f16x8*)(os + roff[kk]);
+      const f16x8 bk = *(const f16x8*)(krow + roff[kk]);
+      const f16x8 bv = *(const f16x8*)(vrow + roff[kk]);
+      s = mfma_f16(aq, bk, s);
+      dp = mfma_f16(ao, bv, dp);
+      // Bound the look-ahead of the fragment reads: two k-steps in flight keep
+      // the register budget at two waves per SIMD (the other wave hides latency).
+      if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
     // Accumulator rows: query q0 + 8 (i/4) + 4 hi + i % 4; lane = key.
     float pv[16], dsv[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 l4 = *(const f32x4*)(nl + 32 * qt + 8 * g + 4 * hi);
-      const f32x4 d4 = *(const f32x4*)(dd + 32 * qt + 8 * g + 4 * hi);
+      const f32x4 l4 = *(const f32x4*)(nl + 8 * g + 4 * hi);
+      const f32x4 d4 = *(const f32x4*)(dd + 8 * g + 4 * hi);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[4 * g + r], c, l4[r]));
@@ -283,53 +306,81 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int rb = (32 * qt + 16 * h2) * ROWB;
+        const int rb = 16 * h2 * ROWB;
         const f16x8 bo = cat4h(lds_read_tr16h(os + rb + toff[dt][0]), lds_read_tr16h(os + rb + toff[dt][1]));
         const f16x8 bq = cat4h(lds_read_tr16h(qs + rb + toff[dt][0]), lds_read_tr16h(qs + rb + toff[dt][1]));
         dv[dt] = mfma_f16(pf[h2], bo, dv[dt]);
         dk[dt] = mfma_f16(df[h2], bq, dk[dt]);
+        if (h2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
   };
 
-  // Ring of NST stages, loads two blocks ahead; block qb0 + i lives in stage i % NST.
-  if (qb0 < nqb) issue_loads(qb0, 0);
-  if (qb0 + 1 < nqb) issue_loads(qb0 + 1, 1);
-  for (int qb = qb0; qb < nqb; ++qb) {
-    const int i = qb - qb0, st = i % NST;
-    if (qb + 1 < nqb) {  // block qb landed; block qb + 1 may still be in flight
-      if (row_loader) wait_vmem_n<2 * NPW + 1>();
-      else wait_vmem_n<2 * NPW>();
+  // Ring of two stages, loads one block ahead; block qb0 + i lives in stage
+  // i % 2. Steps come in pairs so that each stage index is a compile-time
+  // constant (stage base addresses fold into the LDS instruction offsets).
+  auto step = [&](int qb, auto stage_c, auto diag_c) {
+    constexpr int st = decltype(stage_c)::value;
+    constexpr bool diag = decltype(diag_c)::value;
+    wait_vmem();  // this wave's loads of block qb (and, the first time, of the K/V tiles)
+    __syncthreads();
+    if (qb + 1 < nqb) issue_loads(qb + 1, st ^ 1);
+    const int q0 = qb * BQ + 32 * qh;
+    if (diag) {
+      // Tiles whose queries all precede the wave's keys add nothing; tiles
+      // crossing the diagonal are masked element-wise.
+      if (q0 + 31 >= k0w) {
+        if (q0 < k0w + 31) tile(lds[st], q0, std::true_type{});
+        else tile(lds[st], q0, std::false_type{});
+      }
     } else {
-      wait_vmem();
+      tile(lds[st], q0, std::false_type{});
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (qb0 < nqb) issue_loads(qb0, 0);
+  int qb = qb0;
+  if (CAUSAL) {
+    // the (at most) two query blocks that cross the workgroup's keys
+    static_assert(BKV / BQ == 2, "two diagonal query blocks");
+    if (qb < nqb) step(qb++, S0{}, std::true_type{});
+    if (qb < nqb) step(qb++, S1{}, std::true_type{});
+  }
+  for (; qb + 1 < nqb; qb += 2) {
+    step(qb, S0{}, std::false_type{});
+    step(qb + 1, S1{}, std::false_type{});
+  }
+  if (qb < nqb) step(qb, S0{}, std::false_type{});
+
+  // Sum the two query halves of each key group through LDS (the ring is free
+  // once every wave has passed the barrier), then store.
+  // Accumulator layout: lane holds dim 32 dt + col, keys 8 (i/4) + 4 hi + i % 4.
+  float* red = (float*)lds[0];  // [4 key groups][NDT][16][64 lanes]
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16* a = pass == 0 ? dk : dv;
+    if (qh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[((kg * NDT + dt) * 16 + i) * 64 + lane] = a[dt][i];
     }
     __syncthreads();
-    if (qb + 2 < nqb) issue_loads(qb + 2, (i + 2) % NST);
-    const char* sp = lds[st];
-    const int qbase = qb * BQ;
-    if (CAUSAL && qb < qb_unmasked) {
+    if (qh == 0) {
+      float* out = pass == 0 ? dK : dV;
+      const float f = pass == 0 ? scale : 1.f;
 #pragma unroll
-      for (int qt = 0; qt < BQ / 32; ++qt) {
-        const int q0 = qbase + 32 * qt;
-        if (q0 + 31 < k0w) continue;  // every query of the tile precedes every key of the wave
-        tile(sp, qt, q0, q0 < k0w + 31);
-      }
-    } else {
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int qt = 0; qt < BQ / 32; ++qt) tile(sp, qt, qbase + 32 * qt, false);
+        for (int i = 0; i < 16; ++i) {
+          const int kr = k0w + 8 * (i / 4) + 4 * hi + (i % 4);
+          const float v = (a[dt][i] + red[((kg * NDT + dt) * 16 + i) * 64 + lane]) * f;
+          if (kr < N) out[hoff + (size_t)kr * D + 32 * dt + col] = v;
+        }
     }
+    __syncthreads();
   }
-
-  // Accumulator layout: lane holds dim 32 dt + col, keys 8 (i/4) + 4 hi + i % 4.
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kr = k0w + 8 * (i / 4) + 4 * hi + (i % 4);
-      if (kr < N) {
-        dK[hoff + (size_t)kr * D + 32 * dt + col] = dk[dt][i] * scale;
-        dV[hoff + (size_t)kr * D + 32 * dt + col] = dv[dt][i];
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -502,7 +553,7 @@ static hipError_t launch_bwd_d(const void* q, const void* k, const void* v, cons
   if (e != hipSuccess) return e;
   const float c = scale * kLog2e;
   const int nkb = (N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(BH * nkb), dim3(256), 0, st, ws, dk, dv, BH, N, nkb, c,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(BH * nkb), dim3(512), 0, st, ws, dk, dv, BH, N, nkb, c,
                      scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
