@@ -8,11 +8,12 @@
 //   S^T = K Q^T           scaled by scale * s_q * s_k * log2(e) in the exponent
 //   O^T += V^T P^T        P quantised to E4M3, O finished as acc * s_v / l
 // The online softmax is the one of the bf16 kernel (running max m, running
-// denominator l, accumulator rescaled by exp2(m - m_new)). The probabilities
-// are formed as p' = 2^8 * p in [0, 256] before quantisation, which keeps
-// small probabilities clear of E4M3's subnormal range; l sums the unrounded
-// float32 p', so the factor cancels in O = acc / l and lse subtracts 8 in
-// log2 units.
+// denominator l, accumulator rescaled by exp2(m - m_new), lazily: m moves only
+// when a block's max exceeds it by more than 3 in log2 units). The
+// probabilities are formed as p' = 2^5 * exp2(s c - m) <= 2^8 before
+// quantisation, which keeps small probabilities clear of E4M3's subnormal
+// range and large ones under its maximum (448); l sums the unrounded float32
+// p', so the factor cancels in O = acc / l and lse subtracts 5 in log2 units.
 //
 // Operand layouts (per wave, K = 64 contraction per instruction): lane l
 // holds 32 consecutive contraction bytes of row/column l % 32, half-wave
@@ -47,199 +48,217 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <int D, int QT, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+// Swizzle of the 16-byte chunks of an fp8 tile row (D bytes): chunk c of row
+// r is stored at c ^ swz8(r). Keeps the K row reads (two ds_read_b128 per
+// operand, 16 rows at one chunk) and the V transposing reads (8 consecutive
+// rows x 16 bytes) on distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+  if (D == 128) return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);  // 8 chunks per row
+  return (r >> 2) & 3;                                        // 4 chunks per row
+}
+
+// Lazy rescale threshold (log2 units) and the power-of-two scale of P before
+// quantisation: p' = 2^kP8Shift p stays <= 2^(kP8Shift + kTau8) = 256 <= 448.
+constexpr float kTau8 = 3.f;
+constexpr float kP8Shift = 5.f;
+
+// 8 waves x 32 query rows (BR = 256), blocks of BC = 128 keys, two waves per
+// SIMD; K/V tiles HBM -> LDS by DMA into a 2-stage ring.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                          const uint8_t* __restrict__ V, bf16* __restrict__ O,
                                                          float* __restrict__ LSE, const float* __restrict__ descale,
                                                          int BH, int N, int nqb, float scale) {
-  constexpr int BR = 128 * QT;
-  constexpr int KS = D + 16, VS = D + 16;  // LDS row strides (bytes)
-  constexpr int KT = BC * KS, VT = BC * VS;
+  constexpr int NW = 8, BR = 32 * NW, BC = 128;
+  constexpr int ROWB = D, TILEB = BC * ROWB, CPR = D / 16;
+  constexpr int NPW = CPR * BC / 64 / NW;  // 1024-byte DMA instructions per wave per tile
   constexpr int NKT = BC / 32, NDT = D / 32, NKS = D / 64, NPV = BC / 64;
-  constexpr int CHUNKS = BC * D / 16;
-  constexpr int CPT = CHUNKS / 256;
-  static_assert(CHUNKS % 256 == 0 && BC % 64 == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (KT + VT)];
+  static_assert(NPW >= 1, "tile split");
+  __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
 
   int bh, qb;
   map_block8(blockIdx.x, BH, nqb, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
   const size_t hoff = (size_t)bh * N * D;
-  const int q0 = qb * BR + wave * 32 * QT;
+  const int qw = qb * BR + 32 * wave;
+  const int q = qw + col;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const float s_v = descale[2];
   const float c = scale * descale[0] * descale[1] * kLog2e;
 
-  i32x8 qf[QT][NKS];
+  const i32x4 kr = make_rsrc(K + hoff, (unsigned)N * ROWB);
+  const i32x4 vr = make_rsrc(V + hoff, (unsigned)N * ROWB);
+  // DMA: instruction n of this wave fills tile chunks 64 (NPW wave + n) + lane,
+  // i.e. tile row R = p / CPR, physical chunk p % CPR holding logical chunk
+  // (p % CPR) ^ swz8(R). K row R holds key pi(R) (bits 2 and 3 of R swapped);
+  // V row R holds key R.
+  unsigned koff_g[NPW], voff_g[NPW];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int q = q0 + 32 * qt + col;
+  for (int n = 0; n < NPW; ++n) {
+    const int p = 64 * (NPW * wave + n) + lane, R = p / CPR, pc = p % CPR;
+    const int lc = pc ^ swz8<D>(R);
+    koff_g[n] = swap_bits23(R) * ROWB + 16 * lc;
+    voff_g[n] = R * ROWB + 16 * lc;
+  }
+  auto issue_loads = [&](int kb, char* st) {
+    const unsigned base = (unsigned)kb * TILEB;
+    const unsigned la = lds_addr(st) + 1024u * NPW * wave_u;
+#pragma unroll
+    for (int n = 0; n < NPW; ++n) {
+      load_lds16(kr, la + 1024u * n, base + koff_g[n]);
+      load_lds16(vr, la + TILEB + 1024u * n, base + voff_g[n]);
+    }
+  };
+  // K operand reads: row 32 kt + col, bytes 64 kk + 32 hi .. + 31 (chunks 4 kk + 2 hi, + 1).
+  int koff[NKS][2];
+#pragma unroll
+  for (int kk = 0; kk < NKS; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) koff[kk][h] = col * ROWB + 16 * ((4 * kk + 2 * hi + h) ^ swz8<D>(col));
+  // V transposing reads: row 64 u + 16 t + 8 hi + (j >> 1), byte column 32 dt + 16 g + 8 (j & 1).
+  int voff[NDT];
+  {
+    const int j = lane & 15, g = (lane >> 4) & 1;
+    const int r = 8 * hi + (j >> 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) voff[dt] = r * ROWB + 16 * ((2 * dt + g) ^ swz8<D>(r)) + 8 * (j & 1);
+  }
+
+  i32x8 qf[NKS];
+  {
     const i32x4* src = (const i32x4*)(Q + hoff + (size_t)(q < N ? q : 0) * D);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       i32x4 a = src[4 * ks + 2 * hi], b = src[4 * ks + 2 * hi + 1];
       if (q >= N) a = b = i32x4{};
-      qf[qt][ks] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      qf[ks] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
   }
-  f32x16 acc[QT][NDT];
-  float m[QT], l[QT];
+  f32x16 acc[NDT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m[qt] = kNegInf;
-    l[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x16{};
-  }
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+  float m = kNegInf, l = 0.f;
 
   const int nkb_all = (N + BC - 1) / BC;
   const int q_last = min(N - 1, qb * BR + BR - 1);
   const int nkb = CAUSAL ? min(nkb_all, q_last / BC + 1) : nkb_all;
 
-  i32x4 kreg[CPT], vreg[CPT];
-  auto load_regs = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i, row = idx / (D / 16), c16 = idx % (D / 16);
-      const int key = kb * BC + row;
-      const size_t off = hoff + (size_t)(key < N ? key : 0) * D + 16 * c16;  // clamped: always in bounds
-      const i32x4 a = *(const i32x4*)(K + off), b = *(const i32x4*)(V + off);
-      kreg[i] = key < N ? a : i32x4{};
-      vreg[i] = key < N ? b : i32x4{};
-    }
-  };
-  auto store_lds = [&](int buf) {
-    uint8_t* ks = smem + buf * (KT + VT);
-    uint8_t* vs = ks + KT;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + 256 * i, row = idx / (D / 16), c16 = idx % (D / 16);
-      *(i32x4*)(ks + swap_bits23(row) * KS + 16 * c16) = kreg[i];
-      *(i32x4*)(vs + row * VS + 16 * c16) = vreg[i];
-    }
-  };
-
-  load_regs(0);
-  store_lds(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load_regs(kb + 1);
-    const uint8_t* ks = smem + buf * (KT + VT);
-    const uint8_t* vs = ks + KT;
+  auto compute = [&](int kb, const char* st) {
     const int k0 = kb * BC;
-    if (!CAUSAL || k0 <= q0 + 32 * QT - 1) {
-      f32x16 s[QT][NKT];
+    if (CAUSAL && k0 > qw + 31) return;
+    const char* ks = st;
+    const char* vs = st + TILEB;
+    f32x16 s[NKT];
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
+    for (int kt = 0; kt < NKT; ++kt) {
+      s[kt] = f32x16{};
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          const i32x4* src = (const i32x4*)(ks + (32 * kt + col) * KS + 64 * kk + 32 * hi);
-          const i32x4 a0 = src[0], a1 = src[1];
-          const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma_fp8(a, qf[qt][kk], s[qt][kt]);
-        }
+      for (int kk = 0; kk < NKS; ++kk) {
+        const i32x4 a0 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][0]);
+        const i32x4 a1 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][1]);
+        const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        s[kt] = mfma_fp8(a, qf[kk], s[kt]);
       }
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-      i32x8 pf[QT][NPV];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if (need_mask) {
-          const int q = q0 + 32 * qt + col;
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              // accumulator row 8 (i/4) + 4 hi + i % 4 holds key pi(row) = (i & 7) + 8 hi + 16 (i >> 3)
-              const int key = k0 + 32 * kt + (i & 7) + 8 * hi + 16 * (i >> 3);
-              if (key >= N || (CAUSAL && key > q)) s[qt][kt][i] = kNegInf;
-            }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qt][kt][i]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m[qt], mx * c);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m[qt] - m_use);
-        const float shift = 8.f - m_use;  // p' = 2^8 p
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(__builtin_fmaf(s[qt][kt][i], c, shift));
-            s[qt][kt][i] = p;
-            rs += p;
-          }
-        rs += xor32(rs);
-        l[qt] = l[qt] * alpha + rs;
-        m[qt] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
-        // Byte j of the 64-key step u: tile kt = 2u + j / 16, accumulator register j % 16.
-#pragma unroll
-        for (int u = 0; u < NPV; ++u)
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int kt = 2 * u + w / 4, i0 = 4 * (w % 4);
-            pf[qt][u][w] = pack_fp8x4(s[qt][kt][i0], s[qt][kt][i0 + 1], s[qt][kt][i0 + 2], s[qt][kt][i0 + 3]);
-          }
-      }
-      // O^T += V^T P^T. Transposing read t of step u covers V rows 64 u + 16 t + 8 hi + 0..7:
-      // lane j of each 16-lane group reads row (j / 2), bytes 8 (j % 2) .. + 7 of its 16 columns.
-      const int jl = lane & 15, g = (lane >> 4) & 1;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int u = 0; u < NPV; ++u) {
-          i32x8 a;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint8_t* p = vs + (64 * u + 16 * t + 8 * hi + (jl >> 1)) * VS + 32 * dt + 16 * g + 8 * (jl & 1);
-            const i32x2 r = lds_read_tr8(p);
-            a[2 * t] = r[0];
-            a[2 * t + 1] = r[1];
-          }
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma_fp8(a, pf[qt][u], acc[qt][dt]);
-        }
     }
-    if (kb + 1 < nkb) store_lds(buf ^ 1);
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
+      // register i of tile kt holds key k0 + 32 kt + (i & 7) + 8 hi + 16 (i >> 3)
+      const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 8 * hi;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kt + (i & 7) + 16 * (i >> 3) > lim) s[kt][i] = kNegInf;
+    }
+    float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt += 2)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        mx0 = fmaxf(fmaxf(mx0, s[kt][i]), s[kt][i + 1]);
+        mx1 = fmaxf(fmaxf(mx1, s[kt + 1][i]), s[kt + 1][i + 1]);
+      }
+    const float mx = pair_max(fmaxf(mx0, mx1)) * c;
+    const bool upd = mx > m + kTau8;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      const float alpha = upd ? fast_exp2(m - mx) : 1.f;
+      if (upd) m = mx;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    }
+    const float shift = kP8Shift - ((m == kNegInf) ? 0.f : m);  // p' = 2^kP8Shift p
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kt][i], c, shift));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kt][i + 1], c, shift));
+        s[kt][i] = p0;
+        s[kt][i + 1] = p1;
+        rs0 += p0;
+        rs1 += p1;
+      }
+    l += pair_sum(rs0 + rs1);
+    // O^T += V^T P^T, 64-key steps; byte j of step u: tile 2u + j / 16, register j % 16.
+#pragma unroll
+    for (int u = 0; u < NPV; ++u) {
+      i32x8 pf;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kt = 2 * u + w / 4, i0 = 4 * (w % 4);
+        pf[w] = pack_fp8x4(s[kt][i0], s[kt][i0 + 1], s[kt][i0 + 2], s[kt][i0 + 3]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        i32x8 a;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const i32x2 r = lds_read_tr8((const uint8_t*)(vs + (64 * u + 16 * t) * ROWB + voff[dt]));
+          a[2 * t] = r[0];
+          a[2 * t + 1] = r[1];
+        }
+        acc[dt] = mfma_fp8(a, pf, acc[dt]);
+      }
+    }
+  };
+
+  issue_loads(0, lds[0]);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    wait_vmem();
     __syncthreads();
+    if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
+    compute(kb, lds[0]);
+    if (kb + 1 < nkb) {
+      wait_vmem();
+      __syncthreads();
+      if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
+      compute(kb + 1, lds[1]);
+    }
   }
 
+  if (q < N) {
+    const float f = s_v / l;
+    bf16* dst = O + hoff + (size_t)q * D + 4 * hi;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int q = q0 + 32 * qt + col;
-    if (q < N) {
-      const float f = s_v / l[qt];
-      bf16* dst = O + hoff + (size_t)q * D + 4 * hi;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          bf16x4 v = {(bf16)(acc[qt][dt][4 * gg] * f), (bf16)(acc[qt][dt][4 * gg + 1] * f),
-                      (bf16)(acc[qt][dt][4 * gg + 2] * f), (bf16)(acc[qt][dt][4 * gg + 3] * f)};
-          *(bf16x4*)(dst + 32 * dt + 8 * gg) = v;
-        }
-      if (hi == 0) LSE[(size_t)bh * N + q] = (m[qt] + __log2f(l[qt]) - 8.f) * kLn2;
-    }
+      for (int gg = 0; gg < 4; ++gg) {
+        bf16x4 v = {(bf16)(acc[dt][4 * gg] * f), (bf16)(acc[dt][4 * gg + 1] * f), (bf16)(acc[dt][4 * gg + 2] * f),
+                    (bf16)(acc[dt][4 * gg + 3] * f)};
+        *(bf16x4*)(dst + 32 * dt + 8 * gg) = v;
+      }
+    if (hi == 0) LSE[(size_t)bh * N + q] = (m + __log2f(l) - kP8Shift) * kLn2;
   }
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fp8_d(const void* q, const void* k, const void* v, const float* descale, void* o,
                                float* lse, int BH, int N, float scale, hipStream_t st) {
-  constexpr int QT = 1, BC = 64;
-  const int nqb = (N + 128 * QT - 1) / (128 * QT);
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, QT, BC, CAUSAL>), dim3(BH * nqb), dim3(256), 0, st, (const uint8_t*)q,
+  const int nqb = (N + 255) / 256;
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(BH * nqb), dim3(512), 0, st, (const uint8_t*)q,
                      (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, descale, BH, N, nqb, scale);
   return hipGetLastError();
 }
