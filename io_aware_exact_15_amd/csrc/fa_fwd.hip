@@ -28,6 +28,8 @@
 //   * Grid order: heaviest causal query blocks first; all query blocks of a
 //     head go to the same XCD (workgroups are dealt round-robin to the 8
 //     XCDs) so that its K/V stream is shared through one L2.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 #include "../../include/fa.h"
@@ -134,10 +136,18 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   };
 
   // Read addressing (byte offsets inside a tile).
-  int koff[NKS];  // K row (32 kt + col), logical chunk 2 kk + hi; + kt * 32 * ROWB
+  // Offsets are from the start of lds, one set per stage: the second stage
+  // lies beyond the 16-bit immediate offset of LDS reads, and keeping its
+  // bases in registers (hidden from the optimiser, which would otherwise
+  // rebuild them with one vector OR per read) saves that vector work.
+  int koff[2][NKS];  // K row (32 kt + col), logical chunk 2 kk + hi; + kt * 32 * ROWB
 #pragma unroll
-  for (int kk = 0; kk < NKS; ++kk) koff[kk] = col * ROWB + 16 * ((2 * kk + hi) ^ swz<D>(col));
-  int voff[NDT][2];  // V row 4 hi + (j >> 2) + 8 sec, byte column 64 dt + 32 g + 8 (j & 3)
+  for (int kk = 0; kk < NKS; ++kk) {
+    koff[0][kk] = col * ROWB + 16 * ((2 * kk + hi) ^ swz<D>(col));
+    koff[1][kk] = koff[0][kk] + 2 * TILEB;
+    asm volatile("" : "+v"(koff[1][kk]));
+  }
+  int voff[2][NDT][2];  // V row 4 hi + (j >> 2) + 8 sec, byte column 64 dt + 32 g + 8 (j & 3)
   {
     const int j = lane & 15, g = (lane >> 4) & 1;
 #pragma unroll
@@ -146,7 +156,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
       for (int sec = 0; sec < 2; ++sec) {
         const int r = 4 * hi + (j >> 2) + 8 * sec;
         const int bcol = 64 * dt + 32 * g + 8 * (j & 3);
-        voff[dt][sec] = r * ROWB + 16 * ((bcol >> 4) ^ swz<D>(r)) + (bcol & 15);
+        voff[0][dt][sec] = TILEB + r * ROWB + 16 * ((bcol >> 4) ^ swz<D>(r)) + (bcol & 15);
+        voff[1][dt][sec] = voff[0][dt][sec] + 2 * TILEB;
+        asm volatile("" : "+v"(voff[1][dt][sec]));
       }
   }
 
@@ -170,17 +182,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   const int q_last = min(N - 1, qb * BR + BR - 1);
   const int nkb = CAUSAL ? min(nkb_all, q_last / BC + 1) : nkb_all;
 
-  auto compute = [&](int kb, const char* st) {
+  const char* const lb = &lds[0][0];
+  auto compute = [&](int kb, auto stage) {
+    constexpr int S = decltype(stage)::value;
     const int k0 = kb * BC;
     if (CAUSAL && k0 > qw + 31) return;  // every key of the block is after every query of the wave
-    const char* ks = st;
-    const char* vs = st + TILEB;
     f32x16 s[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
       bf16x8 a[NKS];
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) a[kk] = *(const bf16x8*)(ks + koff[kk] + kt * 32 * ROWB);
+      for (int kk = 0; kk < NKS; ++kk) a[kk] = *(const bf16x8*)(lb + koff[S][kk] + kt * 32 * ROWB);
       s[kt] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKS; ++kk) s[kt] = mfma_bf16(a[kk], qf[kk], s[kt]);
@@ -236,8 +248,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int rb = (32 * kt + 16 * h2) * ROWB;
-          const bf16x8 a = cat4(lds_read_tr16((const bf16*)(vs + voff[dt][0] + rb)),
-                                lds_read_tr16((const bf16*)(vs + voff[dt][1] + rb)));
+          const bf16x8 a = cat4(lds_read_tr16((const bf16*)(lb + voff[S][dt][0] + rb)),
+                                lds_read_tr16((const bf16*)(lb + voff[S][dt][1] + rb)));
           acc[dt] = mfma_bf16(a, pf[kt][h2], acc[dt]);
         }
   };
@@ -247,12 +259,12 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     wait_vmem();
     __syncthreads();
     if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
-    compute(kb, lds[0]);
+    compute(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < nkb) {
       wait_vmem();
       __syncthreads();
       if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
-      compute(kb + 1, lds[1]);
+      compute(kb + 1, std::integral_constant<int, 1>{});
     }
   }
 
