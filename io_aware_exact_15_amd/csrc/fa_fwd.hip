@@ -189,13 +189,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     if (CAUSAL && k0 > qw + 31) return;  // every key of the block is after every query of the wave
     f32x16 s[NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      bf16x8 a[NKS];
+    for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
+    // k-step outer: the NKT products of one step are independent, and the
+    // fragment reads of the next step are issued before them (the fences
+    // keep the scheduler from sinking the reads next to their use).
+    bf16x8 a[2][NKT];
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) a[kk] = *(const bf16x8*)(lb + koff[S][kk] + kt * 32 * ROWB);
-      s[kt] = f32x16{};
+    for (int kt = 0; kt < NKT; ++kt) a[0][kt] = *(const bf16x8*)(lb + koff[S][0] + kt * 32 * ROWB);
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) s[kt] = mfma_bf16(a[kk], qf[kk], s[kt]);
+    for (int kk = 0; kk < NKS; ++kk) {
+      if (kk + 1 < NKS) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+          a[(kk + 1) & 1][kt] = *(const bf16x8*)(lb + koff[S][kk + 1] + kt * 32 * ROWB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma_bf16(a[kk & 1][kt], qf[kk], s[kt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
       // key index of register i of tile kt: k0 + 32 kt + 8 (i / 4) + 4 hi + i % 4
@@ -241,17 +252,28 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     l += pair_sum(rs0 + rs1);
     // O^T += V^T P^T; contraction slots per 16-key step: lanes 0-31 keys
     // {0-3, 8-11}, lanes 32-63 keys {4-7, 12-15} (the accumulator rows).
+    // Step outer, as for the scores: the NDT products of a step are
+    // independent and the next step's transposing reads are issued first.
+    constexpr int NST = 2 * NKT;  // 16-key steps per block
+    auto vread = [&](int st, int dt) __attribute__((always_inline)) {
+      const int rb = 16 * st * ROWB;
+      return cat4(lds_read_tr16((const bf16*)(lb + voff[S][dt][0] + rb)),
+                  lds_read_tr16((const bf16*)(lb + voff[S][dt][1] + rb)));
+    };
+    bf16x8 vf[2][NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt) vf[0][dt] = vread(0, dt);
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
+    for (int st = 0; st < NST; ++st) {
+      if (st + 1 < NST) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int rb = (32 * kt + 16 * h2) * ROWB;
-          const bf16x8 a = cat4(lds_read_tr16((const bf16*)(lb + voff[S][dt][0] + rb)),
-                                lds_read_tr16((const bf16*)(lb + voff[S][dt][1] + rb)));
-          acc[dt] = mfma_bf16(a, pf[kt][h2], acc[dt]);
-        }
+        for (int dt = 0; dt < NDT; ++dt) vf[(st + 1) & 1][dt] = vread(st + 1, dt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma_bf16(vf[st & 1][dt], pf[st >> 1][st & 1], acc[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   issue_loads(0, lds[0]);
