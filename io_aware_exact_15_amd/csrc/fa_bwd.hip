@@ -12,11 +12,14 @@
 // Three kernels run in order on the caller's stream:
 //   bwd_prep  per row: fp16 copies of Q, K, V, dO; D = rowsum(dO * O);
 //             -lse * log2(e). Bandwidth-bound, one pass over the inputs.
-//   bwd_dkdv  one workgroup per block of 128 keys (4 waves x 32 keys); K and
-//             V stay in registers, Q / dO tiles and their per-row lse / D
-//             stream HBM -> LDS by DMA. S = Q K^T is formed with keys along
-//             the lanes so that P and dS leave the accumulators already in
-//             the operand layout of dV += P^T dO and dK += dS^T Q.
+//   bwd_dkdv  one workgroup per block of 128 keys, 8 waves: wave w owns keys
+//             32 (w mod 4) .. +31 and the query half w / 4 of every 64-query
+//             block. The K and V tiles stay in LDS for the whole loop; Q / dO
+//             tiles and their per-row lse / D stream HBM -> LDS by DMA. S = Q K^T
+//             is formed with keys along the lanes so that P and dS leave the
+//             accumulators already in the operand layout of dV += P^T dO and
+//             dK += dS^T Q. The two query halves of a key group are summed
+//             through LDS at the end.
 //   bwd_dq    one workgroup per block of 256 queries (8 waves x 32 queries,
 //             two waves per SIMD); Q and dO stay in registers, K / V tiles
 //             stream by DMA; S^T = K Q^T (queries along lanes) so dS^T feeds
@@ -466,19 +469,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
     const char* ks = st;
     const char* vs = st + TILEB;
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
-    // S^T = K Q^T and dP^T = V dO^T for the 32-key tiles of the block.
+    // S^T = K Q^T and dP^T = V dO^T for the 32-key tiles of the block, k-step
+    // outer: the 2 NKT products of a step are independent and the next
+    // step's fragments are read before them (the fences keep the scheduler
+    // from sinking the reads next to their use).
     f32x16 s[NKT], dp[NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      s[kt] = dp[kt] = f32x16{};
+    for (int kt = 0; kt < NKT; ++kt) s[kt] = dp[kt] = f32x16{};
+    f16x8 ak[2][NKT], av[2][NKT];
+    auto kvread = [&](int kk, int b) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) {
-        const f16x8 ak = *(const f16x8*)(ks + 32 * kt * ROWB + roff[kk]);
-        const f16x8 av = *(const f16x8*)(vs + 32 * kt * ROWB + roff[kk]);
-        s[kt] = mfma_f16(ak, qf[kk], s[kt]);
-        dp[kt] = mfma_f16(av, of[kk], dp[kt]);
+      for (int kt = 0; kt < NKT; ++kt) {
+        ak[b][kt] = *(const f16x8*)(ks + 32 * kt * ROWB + roff[kk]);
+        av[b][kt] = *(const f16x8*)(vs + 32 * kt * ROWB + roff[kk]);
       }
+    };
+    kvread(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) {
+      if (kk + 1 < NKS) kvread(kk + 1, (kk + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        s[kt] = mfma_f16(ak[kk & 1][kt], qf[kk], s[kt]);
+        dp[kt] = mfma_f16(av[kk & 1][kt], of[kk], dp[kt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    f16x8 df[NKT][2];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
       float dsv[16];
@@ -490,20 +508,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
         if (need_mask && 8 * (i / 4) + (i % 4) > lim) p = 0.f;
         dsv[i] = p * (dp[kt][i] - dq_d);
       }
-      f16x8 df[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
-        df[h2] = f16x8{(f16)dsv[8 * h2], (f16)dsv[8 * h2 + 1], (f16)dsv[8 * h2 + 2], (f16)dsv[8 * h2 + 3],
-                       (f16)dsv[8 * h2 + 4], (f16)dsv[8 * h2 + 5], (f16)dsv[8 * h2 + 6], (f16)dsv[8 * h2 + 7]};
-      // dQ^T += K^T dS^T: K^T read transposed, key order of the accumulator rows.
+        df[kt][h2] = f16x8{(f16)dsv[8 * h2], (f16)dsv[8 * h2 + 1], (f16)dsv[8 * h2 + 2], (f16)dsv[8 * h2 + 3],
+                           (f16)dsv[8 * h2 + 4], (f16)dsv[8 * h2 + 5], (f16)dsv[8 * h2 + 6], (f16)dsv[8 * h2 + 7]};
+    }
+    // dQ^T += K^T dS^T: K^T read transposed, key order of the accumulator
+    // rows; 16-key steps outer with the next step's reads issued first.
+    constexpr int NST = 2 * NKT;
+    auto kread = [&](int st, int dt) __attribute__((always_inline)) {
+      const int rb = 16 * st * ROWB;
+      return cat4h(lds_read_tr16h(ks + rb + toff[dt][0]), lds_read_tr16h(ks + rb + toff[dt][1]));
+    };
+    f16x8 kf[2][NDT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt) kf[0][dt] = kread(0, dt);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int rb = (32 * kt + 16 * h2) * ROWB;
-          const f16x8 a = cat4h(lds_read_tr16h(ks + rb + toff[dt][0]), lds_read_tr16h(ks + rb + toff[dt][1]));
-          acc[dt] = mfma_f16(a, df[h2], acc[dt]);
-        }
+    for (int st = 0; st < NST; ++st) {
+      if (st + 1 < NST) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) kf[(st + 1) & 1][dt] = kread(st + 1, dt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma_f16(kf[st & 1][dt], df[st >> 1][st & 1], acc[dt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
