@@ -10,6 +10,7 @@ Prints one JSON line. Per-kernel durations come from HIP events recorded on
 the launch stream around every launch of the timed region.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+  python bench.py --configs      # one JSON line per workload and pass (not the bench line)
 """
 import argparse
 import json
@@ -95,12 +96,82 @@ def cpu_baseline(w, rows_per_head=1536):
     }
 
 
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_F32_MFMA_TFLOPS = 157.3
+
+
+def _median_ms(torch, fn, iters, warmup):
+    for _ in range(warmup):
+        fn()
+    ts = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def run_configs(iters=20, warmup=3):
+    """Times every workload of the path (one JSON line per workload and pass)."""
+    import torch
+
+    from io_aware_exact_15_amd import binding as fa
+    from io_aware_exact_15_amd import inputs
+
+    dev = torch.device("cuda:0")
+    for name, w in inputs.WORKLOADS.items():
+        B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+        scale = 1.0 / math.sqrt(d)
+        inp = inputs.make_inputs(B, H, N, d, w["seed"], w["dtype"], with_do=w["backward"])
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+        if w["dtype"] == "fp8":
+            in_t, o_t, peak, odt = fa.FA_FP8_E4M3, fa.FA_BF16, PEAK_FP8_TFLOPS, torch.bfloat16
+            desc = torch.tensor([inp["sq"], inp["sk"], inp["sv"]], dtype=torch.float32, device=dev)
+        elif w["dtype"] == "f32":
+            in_t, o_t, peak, odt, desc = fa.FA_F32, fa.FA_F32, PEAK_F32_MFMA_TFLOPS, torch.float32, None
+        else:
+            in_t, o_t, peak, odt, desc = fa.FA_BF16, fa.FA_BF16, PEAK_BF16_TFLOPS, torch.bfloat16, None
+        if w["backward"]:
+            o_t, odt = fa.FA_F32, torch.float32  # the forward that feeds the backward writes float32 O
+        o = torch.empty(B, H, N, d, dtype=odt, device=dev)
+        for causal in w["causal"]:
+            fwd = lambda: fa.fa_forward_typed(in_t, o_t, q, k, v, desc, o, lse, scale, causal)
+            med, mn = _median_ms(torch, fwd, iters, warmup)
+            f = _flops(B, H, N, d, causal, "fwd")
+            print(json.dumps({"workload": name, "pass": "fwd", "causal": causal, "dtype": w["dtype"],
+                              "ms_median": med, "ms_min": mn, "tflops": f / (med * 1e-3) / 1e12,
+                              "frac_of_peak": f / (med * 1e-3) / 1e12 / peak, "peak_tflops": peak}), flush=True)
+            if w["backward"]:
+                do = inp["do"].to(dev)
+                dq, dk, dv = (torch.empty(B, H, N, d, dtype=torch.float32, device=dev) for _ in range(3))
+                ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+                fwd()
+                bwd = lambda: fa.fa_backward(q, k, v, o, fa.FA_F32, do, lse, dq, dk, dv, ws, scale, causal)
+                bmed, bmn = _median_ms(torch, bwd, iters, warmup)
+                bf = _flops(B, H, N, d, causal, "bwd")
+                print(json.dumps({"workload": name, "pass": "bwd", "causal": causal, "dtype": w["dtype"],
+                                  "ms_median": bmed, "ms_min": bmn, "tflops": bf / (bmed * 1e-3) / 1e12,
+                                  "frac_of_peak": bf / (bmed * 1e-3) / 1e12 / peak, "peak_tflops": peak}),
+                      flush=True)
+                print(json.dumps({"workload": name, "pass": "fwd+bwd", "causal": causal, "dtype": w["dtype"],
+                                  "ms_median": med + bmed,
+                                  "tflops": (f + bf) / ((med + bmed) * 1e-3) / 1e12,
+                                  "frac_of_peak": (f + bf) / ((med + bmed) * 1e-3) / 1e12 / peak}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload (fwd, and bwd where it has one); one JSON line each")
     ap.add_argument("--counters", action="store_true",
                     help="untimed: one float32 copy-kernel launch of known size (512 MiB read + 512 MiB written, "
                          "the traffic calibration) and one step, for hardware-counter runs")
@@ -109,6 +180,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs on a single "
               "MI355X and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.configs:
+        run_configs()
+        return
 
     import torch
 
