@@ -11,6 +11,9 @@ from .attention import (  # noqa: F401
     forward,
     forward_quantized,
     backward,
+    forward_gqa,
+    backward_gqa,
+    forward_decode,
     online_softmax_chunked,
     brute_force_forward,
     brute_force_backward,

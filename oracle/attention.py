@@ -37,6 +37,16 @@ Readings where the pages are silent (each also listed in the design notes):
   * fp8 inputs: the path multiplies E4M3 codes by per-tensor float32 scales;
     the oracle works on the dequantised values code * scale, which float64
     holds exactly.
+  * grouped-query heads: [Blog] (lineage paragraph) pairs the method with
+    grouped-query attention without defining it. Reading: H query heads and
+    Hkv key/value heads, H a multiple of Hkv; query head h uses key/value
+    head floor(h / G) with G = H / Hkv (G consecutive query heads per group).
+    Hkv = H is ordinary multi-head attention, Hkv = 1 multi-query attention.
+  * decode: [Card] (prompts) names the decode step, a few new query rows
+    against a long key/value cache. Reading: the Nq query rows are the last
+    Nq positions of a sequence of Nk keys, so with the causal mask query row
+    i (0-based) sees keys j <= Nk - Nq + i (bottom-right alignment; for
+    Nq = Nk this is the ordinary mask).
 """
 import math
 
@@ -44,6 +54,7 @@ import numpy as np
 
 __all__ = [
     "scores", "probabilities", "forward", "forward_quantized", "backward",
+    "forward_gqa", "backward_gqa", "forward_decode",
     "online_softmax_chunked", "brute_force_forward", "brute_force_backward",
     "decode_e4m3fn",
 ]
@@ -182,6 +193,71 @@ def backward(q, k, v, do, scale, causal, heads=None):
         dq[b, h] = c * (ds @ k[b, h])
         dk[b, h] = c * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def _group(q, k):
+    H, Hkv = q.shape[1], k.shape[1]
+    assert Hkv >= 1 and H % Hkv == 0, "query heads must be a multiple of key/value heads"
+    return H // Hkv
+
+
+def forward_gqa(q, k, v, scale, causal, rows=None):
+    """Grouped-query attention: q [B,H,N,d]; k, v [B,Hkv,N,d].
+
+    Query head h attends with key/value head floor(h / G), G = H / Hkv (the
+    grouped-query reading in the module notes; [Blog] lineage paragraph).
+    Each query head's result is then ordinary attention, so this is
+    `forward` with every key/value head repeated for the G query heads of
+    its group. Returns (O [B,H,R,d], lse [B,H,R]).
+    """
+    k = _f64(k)
+    v = _f64(v)
+    G = _group(q, k)
+    return forward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), scale, causal, rows)
+
+
+def backward_gqa(q, k, v, do, scale, causal):
+    """Gradients of <O, dO> for grouped-query attention.
+
+    A key/value head is an input of the G query heads of its group, so its
+    gradient is the sum of the gradients those heads send it (chain rule for
+    a shared input); dQ is per query head as in `backward`.
+    Returns (dQ [B,H,N,d], dK [B,Hkv,N,d], dV [B,Hkv,N,d]).
+    """
+    k = _f64(k)
+    v = _f64(v)
+    G = _group(q, k)
+    B, Hkv, N, d = k.shape
+    dq, dke, dve = backward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), do, scale, causal)
+    return dq, dke.reshape(B, Hkv, G, N, d).sum(axis=2), dve.reshape(B, Hkv, G, N, d).sum(axis=2)
+
+
+def forward_decode(q, k, v, scale, causal):
+    """Decode step: q [B,H,Nq,d] against a key/value cache k, v [B,Hkv,Nk,d].
+
+    Nq <= Nk new query rows sit at positions Nk - Nq .. Nk - 1 of the
+    sequence (the decode reading in the module notes; [Card] prompts), so
+    with the causal mask row i sees keys j <= Nk - Nq + i. Key/value heads
+    are shared by groups of query heads as in `forward_gqa`. Each row is
+    the full softmax over its visible keys.
+    Returns (O [B,H,Nq,d], lse [B,H,Nq]).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    G = _group(q, k)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    assert 1 <= Nq <= Nk
+    pos = np.arange(Nk - Nq, Nk)
+    out = np.empty((B, H, Nq, v.shape[-1]))
+    lse = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            p, m, l = _softmax_rows(scores(q[b, h], k[b, h // G], scale, causal, pos))
+            out[b, h] = p @ v[b, h // G]
+            lse[b, h] = m + np.log(l)
+    return out, lse
 
 
 def online_softmax_chunked(s_row, v_rows, bounds):

@@ -286,9 +286,124 @@ def pin_quantized_forward(o):
     assert np.max(np.abs(out - ref)) == 0.0 and np.max(np.abs(lse - ref_lse)) == 0.0
 
 
+def _gqa_inputs(seed, B, H, Hkv, Nq, Nk, d):
+    g = _rng(seed)
+    q = g.standard_normal((B, H, Nq, d))
+    k = g.standard_normal((B, Hkv, Nk, d))
+    v = g.standard_normal((B, Hkv, Nk, d))
+    do = g.standard_normal((B, H, Nq, d))
+    return q, k, v, do
+
+
+def pin_gqa_torch(o):
+    """Grouped-query heads: torch's float64 CPU attention with enable_gqa and
+    its autograd (a library implementation of the same head sharing) agree."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, N, d, seed) in ((2, 6, 2, 19, 8, 30), (1, 4, 1, 33, 16, 31), (1, 4, 4, 12, 8, 32)):
+        q, k, v, do = _gqa_inputs(seed, B, H, Hkv, N, N, d)
+        c = float(np.float32(1.0 / math.sqrt(d)))
+        for causal in (False, True):
+            tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+            ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=c, enable_gqa=True)
+            ref.backward(torch.tensor(do))
+            out, lse = o.forward_gqa(q, k, v, c, causal)
+            assert np.max(np.abs(out - ref.detach().numpy())) <= 1e-12
+            dq, dk, dv = o.backward_gqa(q, k, v, do, c, causal)
+            assert dk.shape == k.shape and dv.shape == v.shape
+            assert np.max(np.abs(dq - tq.grad.numpy())) <= 1e-10
+            assert np.max(np.abs(dk - tk.grad.numpy())) <= 1e-10
+            assert np.max(np.abs(dv - tv.grad.numpy())) <= 1e-10
+
+
+def pin_gqa_brute_force(o):
+    """Grouped-query heads against the pure-Python brute force, head by head:
+    query head h uses key/value head h // G; a shared head's gradient is the
+    fsum of what each query head of its group sends it."""
+    B, H, Hkv, N, d = 1, 6, 2, 7, 3
+    G = H // Hkv
+    q, k, v, do = _gqa_inputs(33, B, H, Hkv, N, N, d)
+    for causal in (False, True):
+        c = 0.5
+        out, lse = o.forward_gqa(q, k, v, c, causal)
+        dq, dk, dv = o.backward_gqa(q, k, v, do, c, causal)
+        sk = [[[0.0] * d for _ in range(N)] for _ in range(Hkv)]
+        parts_k = [[[[] for _ in range(d)] for _ in range(N)] for _ in range(Hkv)]
+        parts_v = [[[[] for _ in range(d)] for _ in range(N)] for _ in range(Hkv)]
+        for h in range(H):
+            kv = h // G
+            bo, bl = o.brute_force_forward(q[0, h], k[0, kv], v[0, kv], c, causal)
+            assert np.max(np.abs(out[0, h] - np.array(bo))) <= 1e-12
+            assert np.max(np.abs(lse[0, h] - np.array(bl))) <= 1e-12
+            bq, bk, bv = o.brute_force_backward(q[0, h], k[0, kv], v[0, kv], do[0, h], c, causal)
+            assert np.max(np.abs(dq[0, h] - np.array(bq))) <= 1e-12
+            for j in range(N):
+                for t in range(d):
+                    parts_k[kv][j][t].append(bk[j][t])
+                    parts_v[kv][j][t].append(bv[j][t])
+        for kv in range(Hkv):
+            for j in range(N):
+                for t in range(d):
+                    assert abs(dk[0, kv, j, t] - math.fsum(parts_k[kv][j][t])) <= 1e-12
+                    assert abs(dv[0, kv, j, t] - math.fsum(parts_v[kv][j][t])) <= 1e-12
+
+
+def pin_gqa_finite_differences(o):
+    """Central differences of <O, dO> with respect to a shared K/V head."""
+    B, H, Hkv, N, d = 1, 4, 2, 5, 3
+    q, k, v, do = _gqa_inputs(34, B, H, Hkv, N, N, d)
+    c, h = 0.7, 1e-6
+    for causal in (False, True):
+        _, dk, dv = o.backward_gqa(q, k, v, do, c, causal)
+        f = lambda kk, vv: float(np.sum(o.forward_gqa(q, kk, vv, c, causal)[0] * do))
+        for (kv, j, t) in ((0, 0, 0), (1, 3, 2), (0, 4, 1)):
+            e = np.zeros_like(k)
+            e[0, kv, j, t] = h
+            gk = (f(k + e, v) - f(k - e, v)) / (2 * h)
+            gv = (f(k, v + e) - f(k, v - e)) / (2 * h)
+            assert abs(gk - dk[0, kv, j, t]) <= 1e-6 * max(1.0, abs(gk))
+            assert abs(gv - dv[0, kv, j, t]) <= 1e-6 * max(1.0, abs(gv))
+
+
+def pin_decode_torch(o):
+    """Decode rows: torch's float64 CPU attention with an explicit
+    bottom-right causal mask (row i sees keys j <= Nk - Nq + i) agrees."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, Nq, Nk, d, seed) in ((2, 4, 2, 1, 37, 8, 35), (1, 8, 1, 5, 64, 16, 36), (1, 2, 2, 9, 9, 4, 37)):
+        q, k, v, _ = _gqa_inputs(seed, B, H, Hkv, Nq, Nk, d)
+        c = float(np.float32(1.0 / math.sqrt(d)))
+        for causal in (False, True):
+            tq, tk, tv = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+            mask = None
+            if causal:
+                mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq)
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=c, enable_gqa=True)
+            out, lse = o.forward_decode(q, k, v, c, causal)
+            assert np.max(np.abs(out - ref.numpy())) <= 1e-12
+
+
+def pin_decode_is_tail_of_full(o):
+    """Decode rows are the last rows of the full causal forward; one causal
+    decode row sees every key (so equals the non-causal row)."""
+    B, H, Hkv, N, d = 1, 4, 2, 23, 8
+    q, k, v, _ = _gqa_inputs(38, B, H, Hkv, N, N, d)
+    c = 0.3
+    full, full_lse = o.forward_gqa(q, k, v, c, True)
+    for nq in (1, 4, N):
+        out, lse = o.forward_decode(q[:, :, N - nq:], k, v, c, True)
+        assert np.max(np.abs(out - full[:, :, N - nq:])) <= 1e-12
+        assert np.max(np.abs(lse - full_lse[:, :, N - nq:])) <= 1e-12
+    a, al = o.forward_decode(q[:, :, N - 1:], k, v, c, True)
+    b, bl = o.forward_decode(q[:, :, N - 1:], k, v, c, False)
+    assert np.max(np.abs(a - b)) == 0.0 and np.max(np.abs(al - bl)) == 0.0
+
+
 ALL_PINS = [
     pin_hand_example, pin_rows_sum_to_one, pin_chunked_equals_full, pin_constant_column,
     pin_uniform_scores, pin_brute_force, pin_torch_sdpa, pin_finite_differences,
     pin_single_key, pin_two_keys, pin_permutations, pin_backward_invariants,
     pin_masked_chunk, pin_sampled_rows, pin_e4m3_decode, pin_quantized_forward,
+    pin_gqa_torch, pin_gqa_brute_force, pin_gqa_finite_differences, pin_decode_torch,
+    pin_decode_is_tail_of_full,
 ]

@@ -20,8 +20,12 @@ MUTANTS = {
     "scale_dropped": ("s = c * (q @ k.T)", "s = (q @ k.T)"),
     "causal_off_by_one": ("kj[None, :] <= qi[:, None]", "kj[None, :] < qi[:, None]"),
     "causal_flipped": ("kj[None, :] <= qi[:, None]", "kj[None, :] >= qi[:, None]"),
-    "no_max_shift_lse": ("lse[b, h] = m + np.log(l)", "lse[b, h] = np.log(l)"),
-    "lse_log2": ("lse[b, h] = m + np.log(l)", "lse[b, h] = m + np.log2(l)"),
+    "no_max_shift_lse": ("out[b, h] = p @ v[b, h]\n            lse[b, h] = m + np.log(l)",
+                         "out[b, h] = p @ v[b, h]\n            lse[b, h] = np.log(l)"),
+    "lse_log2": ("out[b, h] = p @ v[b, h]\n            lse[b, h] = m + np.log(l)",
+                 "out[b, h] = p @ v[b, h]\n            lse[b, h] = m + np.log2(l)"),
+    "decode_lse_log2": ("out[b, h] = p @ v[b, h // G]\n            lse[b, h] = m + np.log(l)",
+                        "out[b, h] = p @ v[b, h // G]\n            lse[b, h] = m + np.log2(l)"),
     "pv_transposed_in_dv": ("dv[b, h] = p.T @ do[b, h]", "dv[b, h] = p @ do[b, h]"),
     "missing_D_term": ("ds = p * (dp - dd)", "ds = p * dp"),
     "dk_scale_dropped": ("dk[b, h] = c * (ds.T @ q[b, h])", "dk[b, h] = (ds.T @ q[b, h])"),
@@ -33,6 +37,12 @@ MUTANTS = {
     "e4m3_subnormal": ("sub = sign * mant * 2.0 ** -9", "sub = sign * mant * 2.0 ** -10"),
     "softmax_no_normalise": ("return e / l, m[:, 0], l[:, 0]", "return e, m[:, 0], l[:, 0]"),
     "dequant_scale_dropped": ("q = decode_e4m3fn(qc) * float(np.float32(sq))", "q = decode_e4m3fn(qc)"),
+    "gqa_head_map_modulo": ("return forward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), scale, causal, rows)",
+                            "return forward(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1)), scale, causal, rows)"),
+    "gqa_dk_first_head_only": ("dke.reshape(B, Hkv, G, N, d).sum(axis=2)", "dke.reshape(B, Hkv, G, N, d)[:, :, 0]"),
+    "decode_top_left_mask": ("pos = np.arange(Nk - Nq, Nk)", "pos = np.arange(Nq)"),
+    "decode_head_map_modulo": ("scores(q[b, h], k[b, h // G], scale, causal, pos)",
+                               "scores(q[b, h], k[b, h % k.shape[1]], scale, causal, pos)"),
 }
 
 
