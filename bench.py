@@ -123,10 +123,11 @@ def run_configs(iters=20, warmup=3):
     from io_aware_exact_15_amd import inputs
 
     dev = torch.device("cuda:0")
-    for name, w in inputs.WORKLOADS.items():
-        B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    allw = [(n, dict(w, Hkv=w["H"])) for n, w in inputs.WORKLOADS.items()] + list(inputs.GQA_WORKLOADS.items())
+    for name, w in allw:
+        B, H, Hkv, N, d = w["B"], w["H"], w["Hkv"], w["N"], w["d"]
         scale = 1.0 / math.sqrt(d)
-        inp = inputs.make_inputs(B, H, N, d, w["seed"], w["dtype"], with_do=w["backward"])
+        inp = inputs.make_inputs_heads(B, H, Hkv, N, N, d, w["seed"], w["dtype"], with_do=w["backward"])
         q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
         lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
         if w["dtype"] == "fp8":
@@ -140,7 +141,7 @@ def run_configs(iters=20, warmup=3):
             o_t, odt = fa.FA_F32, torch.float32  # the forward that feeds the backward writes float32 O
         o = torch.empty(B, H, N, d, dtype=odt, device=dev)
         for causal in w["causal"]:
-            fwd = lambda: fa.fa_forward_typed(in_t, o_t, q, k, v, desc, o, lse, scale, causal)
+            fwd = lambda: fa.fa_forward_gqa(in_t, o_t, q, k, v, desc, o, lse, scale, causal)
             med, mn = _median_ms(torch, fwd, iters, warmup)
             f = _flops(B, H, N, d, causal, "fwd")
             print(json.dumps({"workload": name, "pass": "fwd", "causal": causal, "dtype": w["dtype"],
@@ -148,10 +149,11 @@ def run_configs(iters=20, warmup=3):
                               "frac_of_peak": f / (med * 1e-3) / 1e12 / peak, "peak_tflops": peak}), flush=True)
             if w["backward"]:
                 do = inp["do"].to(dev)
-                dq, dk, dv = (torch.empty(B, H, N, d, dtype=torch.float32, device=dev) for _ in range(3))
-                ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+                dq = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+                dk, dv = (torch.empty(B, Hkv, N, d, dtype=torch.float32, device=dev) for _ in range(2))
+                ws = torch.empty(fa.fa_backward_gqa_workspace_bytes(B, H, Hkv, N, d), dtype=torch.uint8, device=dev)
                 fwd()
-                bwd = lambda: fa.fa_backward(q, k, v, o, fa.FA_F32, do, lse, dq, dk, dv, ws, scale, causal)
+                bwd = lambda: fa.fa_backward_gqa(q, k, v, o, fa.FA_F32, do, lse, dq, dk, dv, ws, scale, causal)
                 bmed, bmn = _median_ms(torch, bwd, iters, warmup)
                 bf = _flops(B, H, N, d, causal, "bwd")
                 print(json.dumps({"workload": name, "pass": "bwd", "causal": causal, "dtype": w["dtype"],

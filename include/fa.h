@@ -116,6 +116,45 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, int 
                 void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                 float scale, int causal, void* stream);
 
+/*
+ * fa_forward_gqa -- forward with grouped-query heads. The "FlashAttention"
+ * explainer (A. Tiwari, lineage paragraph) pairs the method with
+ * grouped-query attention: H query heads share Hkv key/value heads, and
+ * query head h attends with key/value head h / (H / Hkv) (groups of
+ * H / Hkv consecutive query heads). Hkv = H is fa_forward_typed; Hkv = 1 is
+ * multi-query attention.
+ *   q, o : [B,H,N,d];  k, v : [B,Hkv,N,d];  lse : float32 [B,H,N].
+ *   Hkv  : >= 1 and a divisor of H, else FA_ERR_INVALID_ARG.
+ * Every other argument, dtype rule and error is that of fa_forward_typed.
+ */
+int fa_forward_gqa(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
+                   const float* descale, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+                   float scale, int causal, void* stream);
+
+/*
+ * fa_backward_gqa_workspace_bytes -- workspace of fa_backward_gqa: two
+ * float32 and fp16 copies of Q and dO per query row, fp16 copies of K and V
+ * per key/value row and, when Hkv < H, float32 per-query-head dK and dV
+ * (B*H*N*d each), every region rounded up to 256 bytes. 0 for an empty
+ * batch, an unsupported head size or an Hkv that does not divide H.
+ */
+size_t fa_backward_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
+
+/*
+ * fa_backward_gqa -- gradients for grouped-query heads (layouts as in
+ * fa_forward_gqa). dq : float32 [B,H,N,d]. dk, dv : float32 [B,Hkv,N,d]: a
+ * key/value head enters the output of each of the H / Hkv query heads that
+ * share it, so its gradient is the sum of what those heads send it. The
+ * per-query-head contributions are formed in the workspace and summed in
+ * head order (deterministic, no atomics).
+ * workspace >= fa_backward_gqa_workspace_bytes(). Every other argument,
+ * rule and error is that of fa_backward.
+ */
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                    const void* dO, const float* lse, float* dq, float* dk, float* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d,
+                    float scale, int causal, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);
 

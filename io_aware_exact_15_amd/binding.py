@@ -25,7 +25,8 @@ FA_FP8_E4M3 = 3
 
 _TORCH_DTYPE = {FA_F32: torch.float32, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.float8_e4m3fn}
 
-EXPORTS = ("fa_forward", "fa_forward_typed", "fa_backward", "fa_backward_workspace_bytes", "fa_status_string")
+EXPORTS = ("fa_forward", "fa_forward_typed", "fa_backward", "fa_backward_workspace_bytes", "fa_forward_gqa",
+           "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_status_string")
 
 
 class FAError(RuntimeError):
@@ -50,6 +51,12 @@ def lib():
         L.fa_backward.restype = i
         L.fa_backward_workspace_bytes.argtypes = [i, i, i, i]
         L.fa_backward_workspace_bytes.restype = sz
+        L.fa_forward_gqa.argtypes = [i, i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.fa_forward_gqa.restype = i
+        L.fa_backward_gqa.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+        L.fa_backward_gqa.restype = i
+        L.fa_backward_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.fa_backward_gqa_workspace_bytes.restype = sz
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -111,6 +118,29 @@ def fa_backward(q, k, v, o, o_dtype, do, lse, dq, dk, dv, workspace, scale, caus
     _check(lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype), _ptr(do), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, N, d, float(scale),
                              int(bool(causal)), _stream(stream)), "fa_backward")
+
+
+def fa_forward_gqa(in_dtype, o_dtype, q, k, v, descale, o, lse, scale, causal, stream=None):
+    """Grouped-query forward: q, o [B,H,N,d]; k, v [B,Hkv,N,d] (Hkv divides H)."""
+    B, H, N, d = _dims(q)
+    Hkv = _dims(k)[1]
+    _check(lib().fa_forward_gqa(int(in_dtype), int(o_dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(descale),
+                                _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale), int(bool(causal)),
+                                _stream(stream)), "fa_forward_gqa")
+
+
+def fa_backward_gqa_workspace_bytes(B, H, Hkv, N, d):
+    return int(lib().fa_backward_gqa_workspace_bytes(int(B), int(H), int(Hkv), int(N), int(d)))
+
+
+def fa_backward_gqa(q, k, v, o, o_dtype, do, lse, dq, dk, dv, workspace, scale, causal, stream=None):
+    """Grouped-query backward: dq [B,H,N,d]; dk, dv [B,Hkv,N,d] summed over each head group."""
+    B, H, N, d = _dims(q)
+    Hkv = _dims(k)[1]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype), _ptr(do), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, Hkv, N, d,
+                                 float(scale), int(bool(causal)), _stream(stream)), "fa_backward_gqa")
 
 
 def fa_status_string(status):

@@ -40,11 +40,12 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
-                     const float* descale, void* o, float* lse, int B, int H, int N, int d,
-                     float scale, int causal, void* stream) {
+int fa_forward_gqa(int in_dtype, int o_dtype, const void* q, const void* k, const void* v, const float* descale,
+                   void* o, float* lse, int B, int H, int Hkv, int N, int d, float scale, int causal,
+                   void* stream) {
   int st = check_shape(B, H, N, d, scale);
   if (st != FA_OK) return st;
+  if (Hkv < 1 || (H > 0 && (Hkv > H || H % Hkv != 0))) return FA_ERR_INVALID_ARG;
   if (in_dtype != FA_F32 && in_dtype != FA_BF16 && in_dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
   if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (in_dtype == FA_FP8_E4M3) {
@@ -56,8 +57,15 @@ int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, co
   if ((long long)B * H == 0) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
-  return fa::launch_forward(in_dtype, o_dtype, q, k, v, descale, o, lse, B, H, N, d, scale, causal,
+  return fa::launch_forward(in_dtype, o_dtype, q, k, v, descale, o, lse, B, H, Hkv, N, d, scale, causal,
                             (hipStream_t)stream);
+}
+
+int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
+                     const float* descale, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, void* stream) {
+  return fa_forward_gqa(in_dtype, o_dtype, q, k, v, descale, o, lse, B, H, H > 0 ? H : 1, N, d, scale, causal,
+                        stream);
 }
 
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
@@ -65,26 +73,39 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   return fa_forward_typed(FA_BF16, FA_BF16, q, k, v, nullptr, o, lse, B, H, N, d, scale, causal, stream);
 }
 
-size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+size_t fa_backward_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
-  return fa::backward_workspace_bytes((size_t)B * H * N, d);
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return 0;
+  return fa::backward_workspace_bytes((size_t)B * H * N, (size_t)B * Hkv * N, d);
 }
 
-int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
-                const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
-                int B, int H, int N, int d, float scale, int causal, void* stream) {
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+  return fa_backward_gqa_workspace_bytes(B, H, H, N, d);
+}
+
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
+                    const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, float scale, int causal, void* stream) {
   int st = check_shape(B, H, N, d, scale);
   if (st != FA_OK) return st;
+  if (Hkv < 1 || (H > 0 && (Hkv > H || H % Hkv != 0))) return FA_ERR_INVALID_ARG;
   if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if ((long long)B * H == 0) return FA_OK;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d) || !aligned16(workspace))
+  if (!workspace || workspace_bytes < fa_backward_gqa_workspace_bytes(B, H, Hkv, N, d) || !aligned16(workspace))
     return FA_ERR_WORKSPACE;
-  return fa::launch_backward(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal,
+  return fa::launch_backward(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, B, H, Hkv, N, d, scale, causal,
                              (hipStream_t)stream);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
+                const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, float scale, int causal, void* stream) {
+  return fa_backward_gqa(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                         H > 0 ? H : 1, N, d, scale, causal, stream);
 }
 
 }  // extern "C"

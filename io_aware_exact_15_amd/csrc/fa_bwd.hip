@@ -12,20 +12,24 @@
 // Three kernels run in order on the caller's stream:
 //   bwd_prep  per row: fp16 copies of Q, K, V, dO; D = rowsum(dO * O);
 //             -lse * log2(e). Bandwidth-bound, one pass over the inputs.
-//   bwd_dkdv  one workgroup per block of 128 keys, 8 waves: wave w owns keys
-//             32 (w mod 4) .. +31 and the query half w / 4 of every 64-query
-//             block. The K and V tiles stay in LDS for the whole loop; Q / dO
-//             tiles and their per-row lse / D stream HBM -> LDS by DMA. S = Q K^T
-//             is formed with keys along the lanes so that P and dS leave the
-//             accumulators already in the operand layout of dV += P^T dO and
-//             dK += dS^T Q. The two query halves of a key group are summed
-//             through LDS at the end.
+//   bwd_dkdv  one workgroup per (query head, block of 128 keys), 8 waves:
+//             wave w owns keys 32 (w mod 4) .. +31 and the query half w / 4
+//             of every 64-query block. The K and V tiles stay in LDS for the
+//             whole loop; Q / dO tiles and their per-row lse / D stream
+//             HBM -> LDS by DMA. S = Q K^T is formed with keys along the lanes
+//             so that P and dS leave the accumulators already in the operand
+//             layout of dV += P^T dO and dK += dS^T Q. The two query halves of
+//             a key group are summed through LDS at the end.
 //   bwd_dq    one workgroup per block of 256 queries (8 waves x 32 queries,
 //             two waves per SIMD); Q and dO stay in registers, K / V tiles
 //             stream by DMA; S^T = K Q^T (queries along lanes) so dS^T feeds
 //             dQ^T += K^T dS^T directly.
-// No buffer of size N x N exists. The workspace holds D, -lse*log2(e) and the
-// fp16 copies ([B,H,N] float32 twice, [B,H,N,d] fp16 four times).
+//   bwd_group_sum  grouped-query heads only: a key/value head shared by G
+//             query heads gets dK, dV = the sum of the G per-query-head
+//             results that bwd_dkdv leaves in the workspace (a fixed order,
+//             so the result is deterministic).
+// No buffer of size N x N exists. The workspace holds D, -lse*log2(e), the
+// fp16 copies and, for grouped heads, the per-query-head dK / dV.
 //
 // Matrix-core operands are fp16: bf16 inputs convert exactly while their
 // magnitude lies in fp16's normal range (2^-14 .. 65504; smaller values keep
@@ -69,43 +73,40 @@ __device__ __forceinline__ int swz_b(int r) {
 
 // Same XCD-aware, heavy-first order as the forward pass; first_is_heavy
 // selects whether block index 0 (dK/dV, causal) or nb-1 (dQ) is heaviest.
-__device__ __forceinline__ void map_block_b(int bid, int BH, int nb, bool first_is_heavy, int& bh, int& blk) {
-  int j;
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, hpx = BH >> 3;
-    j = bid >> 3;
-    bh = xcd + 8 * (j % hpx);
-    j = j / hpx;
-  } else {
-    bh = bid % BH;
-    j = bid / BH;
-  }
-  blk = first_is_heavy ? j : nb - 1 - j;
-}
-
-// Workspace layout (all offsets 256-byte aligned): D [rows] f32,
-// NL = -lse*log2(e) [rows] f32, then Q, K, V, dO as fp16 [rows, d].
+// Workspace layout (all offsets 256-byte aligned): D [q_rows] f32,
+// NL = -lse*log2(e) [q_rows] f32, Q [q_rows, d] fp16, K and V [kv_rows, d]
+// fp16, dO [q_rows, d] fp16, and when q_rows > kv_rows (grouped heads)
+// per-query-head dK and dV [q_rows, d] f32. q_rows = B*H*N, kv_rows = B*Hkv*N.
 struct BwdWs {
   float* Dv;
   float* NL;
   f16 *q, *k, *v, *dO;
+  float *dKp, *dVp;
 };
 static inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
-static inline BwdWs carve_ws(void* base, size_t rows, int d) {
+static inline BwdWs carve_ws(void* base, size_t q_rows, size_t kv_rows, int d) {
   char* p = (char*)base;
   BwdWs w;
-  const size_t fbytes = ws_align(rows * sizeof(float));
-  const size_t hbytes = ws_align(rows * (size_t)d * sizeof(f16));
+  const size_t fbytes = ws_align(q_rows * sizeof(float));
+  const size_t qbytes = ws_align(q_rows * (size_t)d * sizeof(f16));
+  const size_t kvbytes = ws_align(kv_rows * (size_t)d * sizeof(f16));
+  const size_t pbytes = ws_align(q_rows * (size_t)d * sizeof(float));
   w.Dv = (float*)p;
   w.NL = (float*)(p + fbytes);
   w.q = (f16*)(p + 2 * fbytes);
-  w.k = (f16*)(p + 2 * fbytes + hbytes);
-  w.v = (f16*)(p + 2 * fbytes + 2 * hbytes);
-  w.dO = (f16*)(p + 2 * fbytes + 3 * hbytes);
+  w.k = (f16*)(p + 2 * fbytes + qbytes);
+  w.v = (f16*)(p + 2 * fbytes + qbytes + kvbytes);
+  w.dO = (f16*)(p + 2 * fbytes + qbytes + 2 * kvbytes);
+  const bool grouped = q_rows > kv_rows;
+  w.dKp = grouped ? (float*)(p + 2 * fbytes + 2 * qbytes + 2 * kvbytes) : nullptr;
+  w.dVp = grouped ? (float*)(p + 2 * fbytes + 2 * qbytes + 2 * kvbytes + pbytes) : nullptr;
   return w;
 }
-size_t backward_workspace_bytes(size_t rows, int d) {
-  return 2 * ws_align(rows * sizeof(float)) + 4 * ws_align(rows * (size_t)d * sizeof(f16));
+size_t backward_workspace_bytes(size_t q_rows, size_t kv_rows, int d) {
+  size_t b = 2 * ws_align(q_rows * sizeof(float)) + 2 * ws_align(q_rows * (size_t)d * sizeof(f16)) +
+             2 * ws_align(kv_rows * (size_t)d * sizeof(f16));
+  if (q_rows > kv_rows) b += 2 * ws_align(q_rows * (size_t)d * sizeof(float));
+  return b;
 }
 
 // 8 bf16 (raw 16 bytes) -> 8 fp16 (exact in fp16's normal range); f gets the float values.
@@ -129,7 +130,7 @@ template <int D, typename OT>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                        const bf16* __restrict__ V, const bf16* __restrict__ dO,
                                                        const OT* __restrict__ O, const float* __restrict__ LSE,
-                                                       BwdWs ws, long rows) {
+                                                       BwdWs ws, long rows, long kv_rows) {
   constexpr int L = D / 8;
   const long t = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = t / L;
@@ -139,8 +140,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
     const size_t off = (size_t)row * D + 8 * part;
     float tmp[8], dof[8];
     *(f16x8*)(ws.q + off) = bf16x8_to_f16(*(const i32x4*)(Q + off), tmp);
-    *(f16x8*)(ws.k + off) = bf16x8_to_f16(*(const i32x4*)(K + off), tmp);
-    *(f16x8*)(ws.v + off) = bf16x8_to_f16(*(const i32x4*)(V + off), tmp);
+    if (row < kv_rows) {  // key/value heads: kv_rows <= rows
+      *(f16x8*)(ws.k + off) = bf16x8_to_f16(*(const i32x4*)(K + off), tmp);
+      *(f16x8*)(ws.v + off) = bf16x8_to_f16(*(const i32x4*)(V + off), tmp);
+    }
     *(f16x8*)(ws.dO + off) = bf16x8_to_f16(*(const i32x4*)(dO + off), dof);
     const OT* o = O + off;
 #pragma unroll
@@ -158,13 +161,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
 // dK, dV. 8 waves per workgroup of 128 keys: wave w owns key group w % 4
 // (32 keys) and query half w / 4 of every 64-row query block, so two waves
 // share each SIMD and each key group, and each keeps only its own partial
-// dK, dV accumulators (128 registers). K stays in registers as the B
-// operand of S = Q K^T; the workgroup's V tile stays resident in LDS and is
-// read as the B operand of dP = dO V^T. The two partial sums of a key group
-// are added through LDS at the end.
+// dK, dV accumulators (128 registers). The workgroup's K and V tiles stay
+// resident in LDS and are read as the B operands of S = Q K^T and
+// dP = dO V^T. The two partial sums of a key group are added through LDS at
+// the end. With grouped heads the workgroup belongs to one query head and
+// reads its key/value head's K and V.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __restrict__ dK, float* __restrict__ dV,
-                                                          int BH, int N, int nkb, float c, float scale) {
+                                                          int BH, int G, int N, int nkb, float c, float scale) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int ROWB = 2 * D, TILEB = BQ * ROWB, CPR = D / 8;
   constexpr int VTB = BKV * ROWB;           // resident K (and V) tile bytes
@@ -180,19 +184,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
   __shared__ __attribute__((aligned(1024))) char lds[NST][STB];
 
   int bh, kb;
-  map_block_b(blockIdx.x, BH, nkb, CAUSAL, bh, kb);
+  map_head_block(blockIdx.x, BH, G, nkb, CAUSAL, bh, kb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
   const int kg = wave & 3, qh = wave >> 2;  // key group, query half
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * N * D;         // query head: Q, dO; dK, dV written here
+  const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head: K, V
   const int k0w = kb * BKV + 32 * kg;  // first key of this wave
   const int key = k0w + col;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   const i32x4 qr = make_rsrc(ws.q + hoff, (unsigned)N * ROWB);
   const i32x4 orr = make_rsrc(ws.dO + hoff, (unsigned)N * ROWB);
-  const i32x4 vr = make_rsrc(ws.v + hoff, (unsigned)N * ROWB);
-  const i32x4 kr = make_rsrc(ws.k + hoff, (unsigned)N * ROWB);
+  const i32x4 vr = make_rsrc(ws.v + kvoff, (unsigned)N * ROWB);
+  const i32x4 kr = make_rsrc(ws.k + kvoff, (unsigned)N * ROWB);
   const i32x4 nlr = make_rsrc(ws.NL + (size_t)bh * N, (unsigned)N * 4);
   const i32x4 dr = make_rsrc(ws.Dv + (size_t)bh * N, (unsigned)N * 4);
   // DMA addressing: instruction n of this wave fills tile chunks 64 (NP wave + n) + lane.
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
 // ---------------------------------------------------------------------------
 // dQ. 8 waves x 32 queries (BR = 256), two waves per SIMD; key blocks of 64.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restrict__ dQ, int BH, int N, int nqb,
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restrict__ dQ, int BH, int G, int N, int nqb,
                                                         float c, float scale) {
   constexpr int NW = 8, BR = 32 * NW, BC = 64;
   constexpr int ROWB = 2 * D, TILEB = BC * ROWB, CPR = D / 8;
@@ -399,16 +404,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
   __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
 
   int bh, qb;
-  map_block_b(blockIdx.x, BH, nqb, false, bh, qb);
+  map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * N * D;         // query head: Q, dO, dQ
+  const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head: K, V
   const int qw = qb * BR + 32 * wave;
   const int q = qw + col;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  const i32x4 kr = make_rsrc(ws.k + hoff, (unsigned)N * ROWB);
-  const i32x4 vr = make_rsrc(ws.v + hoff, (unsigned)N * ROWB);
+  const i32x4 kr = make_rsrc(ws.k + kvoff, (unsigned)N * ROWB);
+  const i32x4 vr = make_rsrc(ws.v + kvoff, (unsigned)N * ROWB);
   unsigned goff[NPW];
 #pragma unroll
   for (int n = 0; n < NPW; ++n) {
@@ -564,44 +570,70 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Grouped heads: out[kv row] = sum over g < G of part[(kv head * G + g) row],
+// 4 floats per lane, heads added in order g = 0, 1, ...
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                            long head_elems, int G, long total4) {
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total4) return;
+  const long e = 4 * t;                      // element of the [B*Hkv, N, d] output
+  const long kvh = e / head_elems, r = e - kvh * head_elems;
+  const float* src = part + kvh * G * head_elems + r;
+  f32x4 acc = *(const f32x4*)src;
+  for (int g = 1; g < G; ++g) acc += *(const f32x4*)(src + g * head_elems);
+  *(f32x4*)(out + e) = acc;
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
-                               const float* lse, float* dq, float* dk, float* dv, void* workspace, int BH, int N,
-                               float scale, hipStream_t st) {
-  const long rows = (long)BH * N;
-  const BwdWs ws = carve_ws(workspace, (size_t)rows, D);
+                               const float* lse, float* dq, float* dk, float* dv, void* workspace, int BH, int G,
+                               int N, float scale, hipStream_t st) {
+  const long rows = (long)BH * N, kv_rows = rows / G;
+  const BwdWs ws = carve_ws(workspace, (size_t)rows, (size_t)kv_rows, D);
   const long threads = rows * (D / 8);
   const int pre_blocks = (int)((threads + 255) / 256);
   if (o_dtype == FA_F32)
     hipLaunchKernelGGL((bwd_prep_kernel<D, float>), dim3(pre_blocks), dim3(256), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, (const float*)o, lse, ws, rows);
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, (const float*)o, lse, ws, rows, kv_rows);
   else
     hipLaunchKernelGGL((bwd_prep_kernel<D, bf16>), dim3(pre_blocks), dim3(256), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, (const bf16*)o, lse, ws, rows);
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, (const bf16*)o, lse, ws, rows, kv_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float c = scale * kLog2e;
   const int nkb = (N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(BH * nkb), dim3(512), 0, st, ws, dk, dv, BH, N, nkb, c,
-                     scale);
+  float* dk_out = G > 1 ? ws.dKp : dk;  // grouped heads: per-query-head results, summed below
+  float* dv_out = G > 1 ? ws.dVp : dv;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(BH * nkb), dim3(512), 0, st, ws, dk_out, dv_out, BH, G, N,
+                     nkb, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (G > 1) {
+    const long head_elems = (long)N * D, total4 = kv_rows * D / 4;
+    const int blocks = (int)((total4 + 255) / 256);
+    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(blocks), dim3(256), 0, st, ws.dKp, dk, head_elems, G, total4);
+    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(blocks), dim3(256), 0, st, ws.dVp, dv, head_elems, G, total4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int nqb = (N + 255) / 256;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(BH * nqb), dim3(512), 0, st, ws, dq, BH, N, nqb, c, scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(BH * nqb), dim3(512), 0, st, ws, dq, BH, G, N, nqb, c,
+                     scale);
   return hipGetLastError();
 }
 
 int launch_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
-                    const float* lse, float* dq, float* dk, float* dv, void* workspace, int B, int H, int N, int d,
-                    float scale, int causal, hipStream_t stream) {
-  const int BH = B * H;
+                    const float* lse, float* dq, float* dk, float* dv, void* workspace, int B, int H, int Hkv,
+                    int N, int d, float scale, int causal, hipStream_t stream) {
+  const int BH = B * H, G = H / Hkv;
   hipError_t e;
   if (d == 64)
-    e = causal ? launch_bwd_d<64, true>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, N, scale, stream)
-               : launch_bwd_d<64, false>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, N, scale, stream);
+    e = causal ? launch_bwd_d<64, true>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale, stream)
+               : launch_bwd_d<64, false>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale, stream);
   else
-    e = causal ? launch_bwd_d<128, true>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, N, scale, stream)
-               : launch_bwd_d<128, false>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, N, scale, stream);
+    e = causal ? launch_bwd_d<128, true>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale, stream)
+               : launch_bwd_d<128, false>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale,
+                                          stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

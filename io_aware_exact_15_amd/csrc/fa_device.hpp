@@ -96,6 +96,31 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
 }
 
 // LDS address (byte offset inside the workgroup's LDS) of a __shared__ pointer.
+// Workgroup -> (head bh, block blk). Workgroups are dealt round-robin to the
+// 8 XCDs; every query head of a head group (G consecutive query heads that
+// share one key/value head) and all their blocks land on the same XCD, so a
+// key/value head's tiles are read through one L2. heavy_first selects the
+// order of the blocks: j-th wave of workgroups takes block j, or nb - 1 - j.
+__device__ __forceinline__ void map_head_block(int bid, int BH, int G, int nb, bool heavy_first, int& bh, int& blk) {
+  int j;
+  if (((BH / G) & 7) == 0) {
+    const int xcd = bid & 7, hpx = BH >> 3;  // query heads per XCD
+    j = bid >> 3;
+    const int r = j % hpx;
+    bh = (xcd + 8 * (r / G)) * G + r % G;
+    j /= hpx;
+  } else if ((BH & 7) == 0) {
+    const int xcd = bid & 7, hpx = BH >> 3;
+    j = bid >> 3;
+    bh = xcd + 8 * (j % hpx);
+    j /= hpx;
+  } else {
+    bh = bid % BH;
+    j = bid / BH;
+  }
+  blk = heavy_first ? j : nb - 1 - j;
+}
+
 __device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(size_t)(const FA_LDS void*)p; }
 
 // 16 bytes per lane from buffer byte offset `voff` straight into LDS (LDS DMA):

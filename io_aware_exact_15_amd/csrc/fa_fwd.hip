@@ -38,17 +38,6 @@ namespace fa {
 
 // Maps the linear workgroup id to (bh, qb): heavy-first query blocks, and
 // when BH is a multiple of 8 every query block of head bh runs on XCD bh % 8.
-__device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int& qb) {
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, j = bid >> 3, hpx = BH >> 3;
-    qb = nqb - 1 - j / hpx;
-    bh = xcd + 8 * (j % hpx);
-  } else {
-    qb = nqb - 1 - bid / BH;
-    bh = bid % BH;
-  }
-}
-
 template <typename T> struct OutStore;
 template <> struct OutStore<bf16> {
   static __device__ __forceinline__ void store4(bf16* dst, float a, float b, float c, float d) {
@@ -93,7 +82,7 @@ __device__ __forceinline__ int swz(int r) {
 template <int D, int BC, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    OutT* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float c) {
+    OutT* __restrict__ O, float* __restrict__ LSE, int BH, int G, int N, int nqb, float c) {
   constexpr int NW = 8, BR = 32 * NW;
   constexpr int NKT = BC / 32;  // 32-key tiles per block
   constexpr int ROWB = 2 * D;          // bytes per tile row
@@ -105,15 +94,16 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
 
   int bh, qb;
-  map_block(blockIdx.x, BH, nqb, bh, qb);
+  map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * N * D;         // query head
+  const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head
   const int qw = qb * BR + 32 * wave;  // first query row of this wave
   const int q = qw + col;
 
-  const i32x4 kr = make_rsrc(K + hoff, (unsigned)N * ROWB);
-  const i32x4 vr = make_rsrc(V + hoff, (unsigned)N * ROWB);
+  const i32x4 kr = make_rsrc(K + kvoff, (unsigned)N * ROWB);
+  const i32x4 vr = make_rsrc(V + kvoff, (unsigned)N * ROWB);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // Load addressing: instruction n of this wave fills tile chunks
@@ -311,7 +301,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
 template <int D, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    OutT* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float c) {
+    OutT* __restrict__ O, float* __restrict__ LSE, int BH, int G, int N, int nqb, float c) {
   constexpr int BR = 128, BC = 32;
   constexpr int KS = D + 4, VS = D + 4;
   constexpr int KT = BC * KS, VT = BC * VS;
@@ -321,10 +311,11 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
   float* vs = smem + KT;
 
   int bh, qb;
-  map_block(blockIdx.x, BH, nqb, bh, qb);
+  map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * N * D;         // query head
+  const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head
   const int q0 = qb * BR + wave * 32;
   const int q = q0 + col;
 
@@ -350,8 +341,8 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
       const int row = idx / (D / 4), c4 = idx % (D / 4), key = k0 + row;
       f32x4 kx = {}, vx = {};
       if (key < N) {
-        kx = *(const f32x4*)(K + hoff + (size_t)key * D + 4 * c4);
-        vx = *(const f32x4*)(V + hoff + (size_t)key * D + 4 * c4);
+        kx = *(const f32x4*)(K + kvoff + (size_t)key * D + 4 * c4);
+        vx = *(const f32x4*)(V + kvoff + (size_t)key * D + 4 * c4);
       }
       *(f32x4*)(ks + row * KS + 4 * c4) = kx;
       *(f32x4*)(vs + row * VS + 4 * c4) = vx;
@@ -410,19 +401,19 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
 
 template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                              int N, float c, hipStream_t st) {
+                              int G, int N, float c, hipStream_t st) {
   const int nqb = (N + 255) / 256;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, 128, CAUSAL, OutT>), dim3(BH * nqb), dim3(512), 0, st, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, N, nqb, c);
+                     (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, G, N, nqb, c);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                             int N, float c, hipStream_t st) {
+                             int G, int N, float c, hipStream_t st) {
   const int nqb = (N + 127) / 128;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, OutT>), dim3(BH * nqb), dim3(256), 0, st, (const float*)q,
-                     (const float*)k, (const float*)v, (OutT*)o, lse, BH, N, nqb, c);
+                     (const float*)k, (const float*)v, (OutT*)o, lse, BH, G, N, nqb, c);
   return hipGetLastError();
 }
 
@@ -431,19 +422,19 @@ static hipError_t launch_f32(const void* q, const void* k, const void* v, void* 
              : ((causal) ? FN<128, true, OT>(__VA_ARGS__) : FN<128, false, OT>(__VA_ARGS__)))
 
 int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
-                   const float* descale, void* o, float* lse, int B, int H, int N, int d, float scale,
-                   int causal, hipStream_t stream) {
-  const int BH = B * H;
+                   const float* descale, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+                   float scale, int causal, hipStream_t stream) {
+  const int BH = B * H, G = H / Hkv;
   const float c = scale * kLog2e;
   hipError_t err;
   if (in_dtype == FA_BF16) {
-    err = (o_dtype == FA_BF16) ? FA_DISPATCH(launch_bf16, d, causal, bf16, q, k, v, o, lse, BH, N, c, stream)
-                               : FA_DISPATCH(launch_bf16, d, causal, float, q, k, v, o, lse, BH, N, c, stream);
+    err = (o_dtype == FA_BF16) ? FA_DISPATCH(launch_bf16, d, causal, bf16, q, k, v, o, lse, BH, G, N, c, stream)
+                               : FA_DISPATCH(launch_bf16, d, causal, float, q, k, v, o, lse, BH, G, N, c, stream);
   } else if (in_dtype == FA_F32) {
-    err = (o_dtype == FA_BF16) ? FA_DISPATCH(launch_f32, d, causal, bf16, q, k, v, o, lse, BH, N, c, stream)
-                               : FA_DISPATCH(launch_f32, d, causal, float, q, k, v, o, lse, BH, N, c, stream);
+    err = (o_dtype == FA_BF16) ? FA_DISPATCH(launch_f32, d, causal, bf16, q, k, v, o, lse, BH, G, N, c, stream)
+                               : FA_DISPATCH(launch_f32, d, causal, float, q, k, v, o, lse, BH, G, N, c, stream);
   } else if (in_dtype == FA_FP8_E4M3 && o_dtype == FA_BF16) {
-    err = launch_forward_fp8(q, k, v, descale, o, lse, BH, N, d, scale, causal, stream);
+    err = launch_forward_fp8(q, k, v, descale, o, lse, BH, G, N, d, scale, causal, stream);
   } else {
     return FA_ERR_UNSUPPORTED;
   }

@@ -31,17 +31,6 @@ namespace fa {
 
 __device__ __forceinline__ int swap_bits23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-__device__ __forceinline__ void map_block8(int bid, int BH, int nqb, int& bh, int& qb) {
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, j = bid >> 3, hpx = BH >> 3;
-    qb = nqb - 1 - j / hpx;
-    bh = xcd + 8 * (j % hpx);
-  } else {
-    qb = nqb - 1 - bid / BH;
-    bh = bid % BH;
-  }
-}
-
 // Packs 4 floats (each in [0, 448]) into 4 E4M3 bytes, round to nearest even.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -69,7 +58,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                          const uint8_t* __restrict__ V, bf16* __restrict__ O,
                                                          float* __restrict__ LSE, const float* __restrict__ descale,
-                                                         int BH, int N, int nqb, float scale) {
+                                                         int BH, int G, int N, int nqb, float scale) {
   constexpr int NW = 8, BR = 32 * NW, BC = 128;
   constexpr int ROWB = D, TILEB = BC * ROWB, CPR = D / 16;
   constexpr int NPW = CPR * BC / 64 / NW;  // 1024-byte DMA instructions per wave per tile
@@ -78,18 +67,19 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
 
   int bh, qb;
-  map_block8(blockIdx.x, BH, nqb, bh, qb);
+  map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * N * D;         // query head
+  const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head
   const int qw = qb * BR + 32 * wave;
   const int q = qw + col;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const float s_v = descale[2];
   const float c = scale * descale[0] * descale[1] * kLog2e;
 
-  const i32x4 kr = make_rsrc(K + hoff, (unsigned)N * ROWB);
-  const i32x4 vr = make_rsrc(V + hoff, (unsigned)N * ROWB);
+  const i32x4 kr = make_rsrc(K + kvoff, (unsigned)N * ROWB);
+  const i32x4 vr = make_rsrc(V + kvoff, (unsigned)N * ROWB);
   // DMA: instruction n of this wave fills tile chunks 64 (NPW wave + n) + lane,
   // i.e. tile row R = p / CPR, physical chunk p % CPR holding logical chunk
   // (p % CPR) ^ swz8(R). K row R holds key pi(R) (bits 2 and 3 of R swapped);
@@ -256,19 +246,19 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fp8_d(const void* q, const void* k, const void* v, const float* descale, void* o,
-                               float* lse, int BH, int N, float scale, hipStream_t st) {
+                               float* lse, int BH, int G, int N, float scale, hipStream_t st) {
   const int nqb = (N + 255) / 256;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(BH * nqb), dim3(512), 0, st, (const uint8_t*)q,
-                     (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, descale, BH, N, nqb, scale);
+                     (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, descale, BH, G, N, nqb, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const float* descale, void* o, float* lse,
-                              int BH, int N, int d, float scale, int causal, hipStream_t st) {
-  if (d == 64) return causal ? launch_fp8_d<64, true>(q, k, v, descale, o, lse, BH, N, scale, st)
-                             : launch_fp8_d<64, false>(q, k, v, descale, o, lse, BH, N, scale, st);
-  return causal ? launch_fp8_d<128, true>(q, k, v, descale, o, lse, BH, N, scale, st)
-                : launch_fp8_d<128, false>(q, k, v, descale, o, lse, BH, N, scale, st);
+                              int BH, int G, int N, int d, float scale, int causal, hipStream_t st) {
+  if (d == 64) return causal ? launch_fp8_d<64, true>(q, k, v, descale, o, lse, BH, G, N, scale, st)
+                             : launch_fp8_d<64, false>(q, k, v, descale, o, lse, BH, G, N, scale, st);
+  return causal ? launch_fp8_d<128, true>(q, k, v, descale, o, lse, BH, G, N, scale, st)
+                : launch_fp8_d<128, false>(q, k, v, descale, o, lse, BH, G, N, scale, st);
 }
 
 }  // namespace fa

@@ -6,24 +6,28 @@
 
 namespace fa {
 
-// Forward launch; arguments already validated by the ABI layer.
+// Forward launch; arguments already validated by the ABI layer. H query
+// heads share Hkv key/value heads (H % Hkv == 0; query head h reads key/value
+// head h / (H / Hkv)).
 int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
-                   const float* descale, void* o, float* lse, int B, int H, int N, int d,
+                   const float* descale, void* o, float* lse, int B, int H, int Hkv, int N, int d,
                    float scale, int causal, hipStream_t stream);
 
-// FP8 E4M3 forward launch (descale: device pointer to {s_q, s_k, s_v}).
+// FP8 E4M3 forward launch (descale: device pointer to {s_q, s_k, s_v});
+// G = query heads per key/value head.
 hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const float* descale, void* o, float* lse,
-                              int BH, int N, int d, float scale, int causal, hipStream_t stream);
+                              int BH, int G, int N, int d, float scale, int causal, hipStream_t stream);
 
 // Backward launch; arguments already validated by the ABI layer. `workspace`
-// holds at least backward_workspace_bytes(B*H*N, d) bytes.
+// holds at least backward_workspace_bytes(B*H*N, B*Hkv*N, d) bytes.
 int launch_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                     const void* dO, const float* lse, float* dq, float* dk, float* dv,
-                    void* workspace, int B, int H, int N, int d, float scale, int causal,
+                    void* workspace, int B, int H, int Hkv, int N, int d, float scale, int causal,
                     hipStream_t stream);
 
-// Backward workspace: D and -lse*log2(e) (float32 per row) and fp16 copies of
-// Q, K, V, dO, each region 256-byte aligned.
-size_t backward_workspace_bytes(size_t rows, int d);
+// Backward workspace: D and -lse*log2(e) (float32 per query row), fp16
+// copies of Q and dO (per query row) and of K and V (per key/value row),
+// each region 256-byte aligned.
+size_t backward_workspace_bytes(size_t q_rows, size_t kv_rows, int d);
 
 }  // namespace fa

@@ -14,6 +14,10 @@ Recipe (the five workloads of the exact-attention path):
     s = amax|x| / 448 and codes e4m3fn(x / s) rounded to nearest even.
   * Sampled rows: per (b, h), `sorted(default_rng([seed, b, h]).choice(N,
     size, replace=False))`.
+  * Grouped-query workloads: Q [B,H,N,d], then K and V [B,Hkv,N,d], then dO
+    [B,H,N,d], drawn in that order from one generator seeded with the
+    workload's seed (same casts as above).
+  * Decode workloads: Q [B,H,Nq,d], then K and V [B,Hkv,Nk,d], same recipe.
 """
 import numpy as np
 import torch
@@ -32,6 +36,15 @@ WORKLOADS = {
                                              sample=None, backward=True),
     "fwd_fp8_causal_b1h8_n65536_d128": dict(seed=5, B=1, H=8, N=65536, d=128, dtype="fp8", causal=(True,),
                                             sample=256, backward=False),
+}
+
+# Grouped-query workloads: the 16K forward and the 4K backward shapes above
+# with 4 query heads per key/value head.
+GQA_WORKLOADS = {
+    "fwd_bf16_gqa_causal_b1h32kv8_n16384_d128": dict(seed=6, B=1, H=32, Hkv=8, N=16384, d=128, dtype="bf16",
+                                                     causal=(True,), sample=512, backward=False),
+    "bwd_bf16_gqa_causal_b2h16kv4_n4096_d128": dict(seed=7, B=2, H=16, Hkv=4, N=4096, d=128, dtype="bf16",
+                                                    causal=(True,), sample=None, backward=True),
 }
 
 
@@ -80,6 +93,33 @@ def make_inputs(B, H, N, d, seed, dtype, with_do=False):
     else:
         raise ValueError(f"unknown dtype {dtype}")
     return out
+
+
+def _cast(out, names, xs, dtype):
+    if dtype == "f32":
+        out.update(zip(names, xs))
+    elif dtype == "bf16":
+        out.update((n, x.to(torch.bfloat16)) for n, x in zip(names, xs))
+    elif dtype == "fp8":
+        for n, x in zip(names, xs):
+            if n == "do":
+                out[n] = x.to(torch.bfloat16)
+                continue
+            codes, s = quantize_e4m3(x)
+            out[n] = codes
+            out["s" + n] = s
+    else:
+        raise ValueError(f"unknown dtype {dtype}")
+    return out
+
+
+def make_inputs_heads(B, H, Hkv, Nq, Nk, d, seed, dtype, with_do=False):
+    """Seeded CPU inputs with H query heads of Nq rows and Hkv key/value heads
+    of Nk rows (grouped-query and decode workloads). Same dict as make_inputs."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    shapes = [(B, H, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)] + ([(B, H, Nq, d)] if with_do else [])
+    xs = [torch.randn(*sh, dtype=torch.float32, generator=g) for sh in shapes]
+    return _cast({}, ["q", "k", "v", "do"][: len(xs)], xs, dtype)
 
 
 def sample_rows(seed, B, H, N, size):

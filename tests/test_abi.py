@@ -95,3 +95,58 @@ def test_workspace_size():
 ])
 def test_backward_validation(kw, status):
     assert _bwd(**kw) == status
+
+
+def _fwd_gqa(**kw):
+    a = dict(in_dtype=fa.FA_BF16, o_dtype=fa.FA_BF16, q=16, k=16, v=16, descale=None, o=16, lse=16,
+             B=1, H=8, Hkv=2, N=8, d=64, scale=0.125, causal=0)
+    a.update(kw)
+    return fa.lib().fa_forward_gqa(a["in_dtype"], a["o_dtype"], a["q"], a["k"], a["v"], a["descale"], a["o"],
+                                   a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["d"], ctypes.c_float(a["scale"]),
+                                   a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),   # does not divide H
+    (dict(Hkv=16), fa.FA_ERR_INVALID_ARG),  # more key/value heads than query heads
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),  # descale missing
+    (dict(H=0, Hkv=1), fa.FA_OK),
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),
+])
+def test_forward_gqa_validation(kw, status):
+    assert _fwd_gqa(**kw) == status
+
+
+def test_gqa_workspace_size():
+    q_rows, kv_rows = 2 * 16 * 4096, 2 * 4 * 4096
+    assert fa.fa_backward_gqa_workspace_bytes(2, 16, 4, 4096, 128) == \
+        2 * q_rows * 4 + 2 * q_rows * 128 * 2 + 2 * kv_rows * 128 * 2 + 2 * q_rows * 128 * 4
+    assert fa.fa_backward_gqa_workspace_bytes(2, 16, 16, 4096, 128) == fa.fa_backward_workspace_bytes(2, 16, 4096, 128)
+    assert fa.fa_backward_gqa_workspace_bytes(1, 6, 4, 64, 64) == 0  # 4 does not divide 6
+    assert fa.fa_backward_gqa_workspace_bytes(1, 6, 0, 64, 64) == 0
+
+
+def _bwd_gqa(ws_bytes=None, **kw):
+    a = dict(q=16, k=16, v=16, o=16, o_dtype=fa.FA_F32, do=16, lse=16, dq=16, dk=16, dv=16, ws=16,
+             B=1, H=4, Hkv=2, N=40, d=128, scale=0.1, causal=1)
+    a.update(kw)
+    need = fa.fa_backward_gqa_workspace_bytes(a["B"], a["H"], a["Hkv"], a["N"], a["d"])
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return fa.lib().fa_backward_gqa(a["q"], a["k"], a["v"], a["o"], a["o_dtype"], a["do"], a["lse"], a["dq"],
+                                    a["dk"], a["dv"], a["ws"], ws_bytes, a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                                    ctypes.c_float(a["scale"]), a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=64), fa.FA_ERR_WORKSPACE),
+    (dict(B=0, q=None), fa.FA_OK),
+])
+def test_backward_gqa_validation(kw, status):
+    assert _bwd_gqa(**kw) == status

@@ -1,0 +1,152 @@
+"""Grouped-query heads: fa_forward_gqa / fa_backward_gqa through the C ABI vs
+the float64 oracle (query head h uses key/value head h // (H / Hkv))."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_exact_15_amd import binding as fa
+from io_aware_exact_15_amd import inputs
+from parity import FA_DT, assert_close, assert_lse, gather_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_forward_gqa(inp, dtype, causal, o_dtype="bf16"):
+    B, H, N, d = inp["q"].shape
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty(B, H, N, d, dtype=torch.bfloat16 if o_dtype == "bf16" else torch.float32, device=dev)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    descale = None
+    if dtype == "fp8":
+        descale = torch.tensor([inp["sq"], inp["sk"], inp["sv"]], dtype=torch.float32, device=dev)
+    fa.fa_forward_gqa(FA_DT[dtype], FA_DT[o_dtype], qd, kd, vd, descale, o, lse, scale, causal)
+    torch.cuda.synchronize()
+    return o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+def _values(inp, dtype):
+    if dtype == "fp8":
+        return [oracle.decode_e4m3fn(inputs.to_numpy(inp[n])) * float(np.float32(inp["s" + n])) for n in "qkv"]
+    return [inputs.to_numpy(inp[n]) for n in "qkv"]
+
+
+def _check_fwd(B, H, Hkv, N, d, seed, dtype, causal, o_dtype="bf16", sample=None):
+    print(f"case B={B} H={H} Hkv={Hkv} N={N} d={d} seed={seed} {dtype} causal={causal} o={o_dtype}", flush=True)
+    inp = inputs.make_inputs_heads(B, H, Hkv, N, N, d, seed, dtype)
+    o, lse = gpu_forward_gqa(inp, dtype, causal, o_dtype)
+    rows = None if sample is None else inputs.sample_rows(seed, B, H, N, sample)
+    ro, rl = oracle.forward_gqa(*_values(inp, dtype), 1.0 / math.sqrt(d), causal, rows)
+    if rows is not None:
+        o, lse = gather_rows(o, rows), gather_rows(lse, rows)
+    tol_dtype = "f32" if (dtype == "f32" and o_dtype == "f32") else ("fp8" if dtype == "fp8" else "bf16")
+    mx, rms = assert_close(o, ro, tol_dtype, "O", o_bf16=(o_dtype == "bf16"))
+    lmx = assert_lse(lse, rl, "lse")
+    print(f"  O max={mx:.3g} rms={rms:.3g} lse={lmx:.3g}", flush=True)
+
+
+def test_workload_fwd_gqa_16k():
+    """B=1 H=32 Hkv=8 N=16384 d=128 causal bf16, 512 seeded rows per query head."""
+    w = inputs.GQA_WORKLOADS["fwd_bf16_gqa_causal_b1h32kv8_n16384_d128"]
+    _check_fwd(w["B"], w["H"], w["Hkv"], w["N"], w["d"], w["seed"], "bf16", True, sample=w["sample"])
+
+
+FWD_EDGE = [
+    (1, 4, 1, 1, 64), (1, 4, 2, 17, 128), (2, 6, 3, 100, 64), (1, 8, 2, 257, 128), (1, 8, 8, 129, 64),
+    (2, 16, 4, 300, 128), (1, 32, 8, 640, 128), (1, 16, 1, 255, 64), (2, 8, 1, 1000, 128),
+]
+
+
+@pytest.mark.parametrize("shape", FWD_EDGE, ids=[f"B{b}H{h}kv{g}N{n}d{d}" for b, h, g, n, d in FWD_EDGE])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_edge_bf16(shape, causal):
+    B, H, Hkv, N, d = shape
+    _check_fwd(B, H, Hkv, N, d, 600 + N, "bf16", causal)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 100, 64), (2, 8, 2, 257, 128)], ids=["small", "ragged"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_edge_f32(shape, causal):
+    B, H, Hkv, N, d = shape
+    _check_fwd(B, H, Hkv, N, d, 700 + N, "f32", causal, o_dtype="f32")
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 300, 128), (1, 16, 4, 1000, 64), (1, 4, 1, 129, 128)],
+                         ids=["kv2", "kv4", "mqa"])
+def test_fwd_edge_fp8(shape):
+    B, H, Hkv, N, d = shape
+    _check_fwd(B, H, Hkv, N, d, 800 + N, "fp8", True)
+
+
+def test_fwd_gqa_equals_repeated_heads():
+    """Independent of the oracle: the grouped call equals the ordinary call on
+    key/value heads repeated for every query head, bit for bit."""
+    B, H, Hkv, N, d = 1, 8, 2, 700, 128
+    inp = inputs.make_inputs_heads(B, H, Hkv, N, N, d, 41, "bf16")
+    o1, l1 = gpu_forward_gqa(inp, "bf16", True)
+    rep = dict(q=inp["q"], k=inp["k"].repeat_interleave(H // Hkv, dim=1).contiguous(),
+               v=inp["v"].repeat_interleave(H // Hkv, dim=1).contiguous())
+    o2, l2 = gpu_forward_gqa(rep, "bf16", True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def gpu_backward_gqa(inp, causal):
+    B, H, N, d = inp["q"].shape
+    Hkv = inp["k"].shape[1]
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    fa.fa_forward_gqa(fa.FA_BF16, fa.FA_F32, qd, kd, vd, None, o, lse, scale, causal)
+    ws = torch.empty(max(fa.fa_backward_gqa_workspace_bytes(B, H, Hkv, N, d), 1), dtype=torch.uint8, device=dev)
+    dq = torch.full((B, H, N, d), float("nan"), dtype=torch.float32, device=dev)
+    dk, dv = (torch.full((B, Hkv, N, d), float("nan"), dtype=torch.float32, device=dev) for _ in range(2))
+    fa.fa_backward_gqa(qd, kd, vd, o, fa.FA_F32, dod, lse, dq, dk, dv, ws, scale, causal)
+    torch.cuda.synchronize()
+    return tuple(t.cpu().to(torch.float64).numpy() for t in (dq, dk, dv))
+
+
+def _check_bwd(B, H, Hkv, N, d, seed, causal):
+    print(f"case bwd B={B} H={H} Hkv={Hkv} N={N} d={d} seed={seed} causal={causal}", flush=True)
+    inp = inputs.make_inputs_heads(B, H, Hkv, N, N, d, seed, "bf16", with_do=True)
+    got = gpu_backward_gqa(inp, causal)
+    ref = oracle.backward_gqa(*(inputs.to_numpy(inp[n]) for n in ("q", "k", "v", "do")), 1.0 / math.sqrt(d), causal)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.all(np.isfinite(g)), name
+        mx, rms = assert_close(g, r, "bf16", name)
+        print(f"  {name}: max={mx:.3g} rms={rms:.3g}", flush=True)
+    return got, inp
+
+
+def test_workload_bwd_gqa_4k():
+    """B=2 H=16 Hkv=4 N=4096 d=128 causal: every element of dQ, dK, dV."""
+    w = inputs.GQA_WORKLOADS["bwd_bf16_gqa_causal_b2h16kv4_n4096_d128"]
+    _check_bwd(w["B"], w["H"], w["Hkv"], w["N"], w["d"], w["seed"], True)
+
+
+BWD_EDGE = [(1, 4, 1, 1, 64), (1, 4, 2, 17, 128), (2, 6, 3, 100, 64), (1, 8, 2, 257, 128), (1, 16, 1, 300, 64),
+            (2, 16, 4, 129, 128)]
+
+
+@pytest.mark.parametrize("shape", BWD_EDGE, ids=[f"B{b}H{h}kv{g}N{n}d{d}" for b, h, g, n, d in BWD_EDGE])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_edge(shape, causal):
+    B, H, Hkv, N, d = shape
+    _check_bwd(B, H, Hkv, N, d, 900 + N, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_gqa_invariants(causal):
+    """Independent of the oracle: per key/value head, sum_j dK_j = 0 and
+    sum_j dV_j = sum over the group's query heads of sum_i dO_i."""
+    B, H, Hkv, N, d = 1, 8, 2, 1200, 128
+    inp = inputs.make_inputs_heads(B, H, Hkv, N, N, d, 42, "bf16", with_do=True)
+    dq, dk, dv = gpu_backward_gqa(inp, causal)
+    do = inp["do"].double().numpy().reshape(B, Hkv, H // Hkv, N, d)
+    assert np.max(np.abs(dk.sum(axis=2))) <= 5e-2
+    assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=(2, 3)))) <= 1e-1
