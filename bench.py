@@ -166,6 +166,31 @@ def run_configs(iters=20, warmup=3):
                                   "frac_of_peak": (f + bf) / ((med + bmed) * 1e-3) / 1e12 / peak}), flush=True)
 
 
+def run_decode_configs(iters=20, warmup=3):
+    """Times the decode workloads (HBM-bound: reported as GB/s of the
+    algorithmic bytes, the K/V cache read once plus Q, O and lse)."""
+    import torch
+
+    from io_aware_exact_15_amd import binding as fa
+    from io_aware_exact_15_amd import inputs
+
+    dev = torch.device("cuda:0")
+    for name, w in inputs.DECODE_WORKLOADS.items():
+        B, H, Hkv, Nq, Nk, d = w["B"], w["H"], w["Hkv"], w["Nq"], w["Nk"], w["d"]
+        inp = inputs.make_inputs_heads(B, H, Hkv, Nq, Nk, d, w["seed"], "bf16")
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o = torch.empty(B, H, Nq, d, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, H, Nq, dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d), dtype=torch.uint8, device=dev)
+        fn = lambda: fa.fa_decode(q, k, v, o, fa.FA_BF16, lse, ws, 1.0 / math.sqrt(d), w["causal"])
+        med, mn = _median_ms(torch, fn, iters, warmup)
+        nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
+        gbs = nbytes / (med * 1e-3) / 1e9
+        print(json.dumps({"workload": name, "pass": "decode", "causal": w["causal"], "dtype": "bf16",
+                          "ms_median": med, "ms_min": mn, "algorithmic_bytes": nbytes, "GB_per_s": gbs,
+                          "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +210,7 @@ def main():
 
     if args.configs:
         run_configs()
+        run_decode_configs()
         return
 
     import torch

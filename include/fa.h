@@ -155,6 +155,36 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
                     void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d,
                     float scale, int causal, void* stream);
 
+/*
+ * fa_decode_workspace_bytes -- workspace of fa_decode: per split of the keys
+ * and per wave, an unnormalised 32 x d float32 partial output and its running
+ * max and denominator; 0 for invalid sizes (see fa_decode).
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
+
+/*
+ * fa_decode -- decode step: Nq new query rows per head against a key/value
+ * cache of Nk rows (the decode step named in the prompts of the card
+ * "FlashAttention Kernel & Online Softmax"), computed as a split-K forward:
+ * each split of the keys keeps its own running max, denominator and output
+ * (the online softmax of the card's definition paragraph) and a second
+ * kernel merges the splits with the same rescale-and-add.
+ *   q     : bf16 [B,H,Nq,d];   k, v : bf16 [B,Hkv,Nk,d] (Hkv divides H; query
+ *           head h uses key/value head h / (H / Hkv)).
+ *   o     : [B,H,Nq,d], o_dtype FA_BF16 or FA_F32, fully overwritten.
+ *   lse   : float32 [B,H,Nq], natural log-sum-exp of the scaled scores.
+ *   causal: the query rows are the last Nq positions of the sequence, so row
+ *           i sees keys j <= Nk - Nq + i; causal = 0 lets every row see all
+ *           Nk keys.
+ *   workspace : device buffer of at least fa_decode_workspace_bytes().
+ * Requires 1 <= Nq <= Nk (else FA_ERR_INVALID_ARG), d in {64, 128}, and
+ * Nk * d * 2 < 2^32 (FA_ERR_UNSUPPORTED otherwise). Other conventions as
+ * for the forward pass.
+ */
+int fa_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+              void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d,
+              float scale, int causal, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);
 

@@ -26,7 +26,8 @@ FA_FP8_E4M3 = 3
 _TORCH_DTYPE = {FA_F32: torch.float32, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.float8_e4m3fn}
 
 EXPORTS = ("fa_forward", "fa_forward_typed", "fa_backward", "fa_backward_workspace_bytes", "fa_forward_gqa",
-           "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_status_string")
+           "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_decode_workspace_bytes", "fa_decode",
+           "fa_status_string")
 
 
 class FAError(RuntimeError):
@@ -57,6 +58,10 @@ def lib():
         L.fa_backward_gqa.restype = i
         L.fa_backward_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_backward_gqa_workspace_bytes.restype = sz
+        L.fa_decode.argtypes = [vp, vp, vp, vp, i, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
+        L.fa_decode.restype = i
+        L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.fa_decode_workspace_bytes.restype = sz
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -141,6 +146,19 @@ def fa_backward_gqa(q, k, v, o, o_dtype, do, lse, dq, dk, dv, workspace, scale, 
     _check(lib().fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype), _ptr(do), _ptr(lse),
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, Hkv, N, d,
                                  float(scale), int(bool(causal)), _stream(stream)), "fa_backward_gqa")
+
+
+def fa_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d):
+    return int(lib().fa_decode_workspace_bytes(int(B), int(H), int(Hkv), int(Nq), int(Nk), int(d)))
+
+
+def fa_decode(q, k, v, o, o_dtype, lse, workspace, scale, causal, stream=None):
+    """Decode step: q, o [B,H,Nq,d]; k, v [B,Hkv,Nk,d] cache; lse [B,H,Nq]."""
+    B, H, Nq, d = _dims(q)
+    Hkv, Nk = _dims(k)[1], _dims(k)[2]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype), _ptr(lse), _ptr(workspace), nbytes,
+                           B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(stream)), "fa_decode")
 
 
 def fa_status_string(status):

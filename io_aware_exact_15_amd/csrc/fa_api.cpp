@@ -108,4 +108,32 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, int 
                          H > 0 ? H : 1, N, d, scale, causal, stream);
 }
 
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk < Nq || (d != 64 && d != 128)) return 0;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return 0;
+  return fa::decode_workspace_bytes(B, H, Hkv, Nq, Nk, d);
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* workspace,
+              size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+              void* stream) {
+  if (B < 0 || H < 0 || Nq < 1 || Nk < Nq) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (Hkv < 1 || (H > 0 && (Hkv > H || H % Hkv != 0))) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  // One head of K or V must be addressable by a 32-bit buffer offset; the
+  // grid (at most one workgroup per 128 keys per row tile) must fit an int.
+  if ((long long)Nk * d * 2 > 0xffffffffLL) return FA_ERR_UNSUPPORTED;
+  const long long R = (long long)(H > 0 ? H / Hkv : 0) * Nq;
+  if ((long long)B * Hkv * ((R + 31) / 32) * ((Nk + 127) / 128) > INT_MAX) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d) || !aligned16(workspace))
+    return FA_ERR_WORKSPACE;
+  return fa::launch_decode(q, k, v, o, o_dtype, lse, workspace, B, H, Hkv, Nq, Nk, d, scale, causal,
+                           (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -95,7 +95,6 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
   return i32x4{(int)(unsigned)b, (int)((unsigned)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-// LDS address (byte offset inside the workgroup's LDS) of a __shared__ pointer.
 // Workgroup -> (head bh, block blk). Workgroups are dealt round-robin to the
 // 8 XCDs; every query head of a head group (G consecutive query heads that
 // share one key/value head) and all their blocks land on the same XCD, so a
@@ -121,6 +120,7 @@ __device__ __forceinline__ void map_head_block(int bid, int BH, int G, int nb, b
   blk = heavy_first ? j : nb - 1 - j;
 }
 
+// LDS address (byte offset inside the workgroup's LDS) of a __shared__ pointer.
 __device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(size_t)(const FA_LDS void*)p; }
 
 // 16 bytes per lane from buffer byte offset `voff` straight into LDS (LDS DMA):

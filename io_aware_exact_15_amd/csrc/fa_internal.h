@@ -30,4 +30,13 @@ int launch_backward(const void* q, const void* k, const void* v, const void* o, 
 // each region 256-byte aligned.
 size_t backward_workspace_bytes(size_t q_rows, size_t kv_rows, int d);
 
+// Decode (split-K) launch; arguments already validated. q [B,H,Nq,d],
+// k, v [B,Hkv,Nk,d]; workspace >= decode_workspace_bytes(...).
+int launch_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* workspace,
+                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
+
+// Decode workspace: per split and wave, the unnormalised partial output
+// (32 x d float32) and its running max and denominator (2 x 32 float32).
+size_t decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
+
 }  // namespace fa

@@ -69,6 +69,16 @@ def quantize_e4m3(x):
     return codes, np.float32(scale.item())
 
 
+# Decode workloads: Nq new rows per query head against an Nk-row cache of
+# Hkv key/value heads (4 query heads per key/value head).
+DECODE_WORKLOADS = {
+    "decode_bf16_b8h32kv8_nq1_nk32768_d128": dict(seed=8, B=8, H=32, Hkv=8, Nq=1, Nk=32768, d=128, dtype="bf16",
+                                                  causal=True),
+    "decode_bf16_b4h32kv8_nq4_nk16384_d128": dict(seed=9, B=4, H=32, Hkv=8, Nq=4, Nk=16384, d=128, dtype="bf16",
+                                                  causal=True),
+}
+
+
 def make_inputs(B, H, N, d, seed, dtype, with_do=False):
     """Seeded CPU inputs of one workload.
 

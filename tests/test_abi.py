@@ -150,3 +150,37 @@ def _bwd_gqa(ws_bytes=None, **kw):
 ])
 def test_backward_gqa_validation(kw, status):
     assert _bwd_gqa(**kw) == status
+
+
+def _dec(ws_bytes=None, **kw):
+    a = dict(q=16, k=16, v=16, o=16, o_dtype=fa.FA_BF16, lse=16, ws=16, B=1, H=8, Hkv=2, Nq=1, Nk=100, d=128,
+             scale=0.1, causal=1)
+    a.update(kw)
+    need = fa.fa_decode_workspace_bytes(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"])
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return fa.lib().fa_decode(a["q"], a["k"], a["v"], a["o"], a["o_dtype"], a["lse"], a["ws"], ws_bytes, a["B"],
+                              a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"],
+                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=101), fa.FA_ERR_INVALID_ARG),  # more new rows than cache rows
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(Nk=1 << 24, Nq=1, d=128), fa.FA_ERR_UNSUPPORTED),  # cache head larger than a 32-bit buffer range
+    (dict(B=0, q=None), fa.FA_OK),
+])
+def test_decode_validation(kw, status):
+    assert _dec(**kw) == status
+
+
+def test_decode_workspace_size():
+    assert fa.fa_decode_workspace_bytes(1, 8, 2, 1, 100, 128) > 0
+    assert fa.fa_decode_workspace_bytes(1, 8, 3, 1, 100, 128) == 0
+    assert fa.fa_decode_workspace_bytes(1, 8, 2, 5, 4, 128) == 0
