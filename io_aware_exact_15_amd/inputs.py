@@ -23,6 +23,7 @@ import numpy as np
 import torch
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 
 # name -> workload description (sizes as in the exact-attention workloads)
 WORKLOADS = {
@@ -69,6 +70,25 @@ def quantize_e4m3(x):
     return codes, np.float32(scale.item())
 
 
+def quantize_e5m2(x):
+    """Per-tensor FP8 E5M2 quantisation: scale = amax|x| / 57344 in float32;
+    codes = e5m2(x / scale), round to nearest even (torch's cast)."""
+    x = x.to(torch.float32)
+    amax = x.abs().max()
+    scale = (amax / E5M2_MAX).to(torch.float32)
+    if float(scale) == 0.0:
+        scale = torch.tensor(1.0, dtype=torch.float32)
+    codes = (x / scale).to(torch.float8_e5m2)
+    return codes, np.float32(scale.item())
+
+
+# FP8 E5M2 variant of the 64K FP8 workload.
+FP8_E5M2_WORKLOADS = {
+    "fwd_fp8e5m2_causal_b1h8_n65536_d128": dict(seed=10, B=1, H=8, N=65536, d=128, dtype="fp8e5m2",
+                                                causal=(True,), sample=256, backward=False),
+}
+
+
 # Decode workloads: Nq new rows per query head against an Nk-row cache of
 # Hkv key/value heads (4 query heads per key/value head).
 DECODE_WORKLOADS = {
@@ -82,27 +102,12 @@ DECODE_WORKLOADS = {
 def make_inputs(B, H, N, d, seed, dtype, with_do=False):
     """Seeded CPU inputs of one workload.
 
-    dtype: "f32" | "bf16" | "fp8". Returns a dict with q, k, v (and do) as
-    CPU tensors of the operand dtype; for "fp8" also the scales sq, sk, sv.
+    dtype: "f32" | "bf16" | "fp8" (E4M3) | "fp8e5m2". Returns a dict with q,
+    k, v (and do) as CPU tensors of the operand dtype; for the FP8 dtypes
+    also the scales sq, sk, sv.
     """
     xs = normal_tensors(B, H, N, d, seed, 4 if with_do else 3)
-    names = ["q", "k", "v", "do"][: len(xs)]
-    out = {}
-    if dtype == "f32":
-        out.update(zip(names, xs))
-    elif dtype == "bf16":
-        out.update((n, x.to(torch.bfloat16)) for n, x in zip(names, xs))
-    elif dtype == "fp8":
-        for n, x in zip(names, xs):
-            if n == "do":
-                out[n] = x.to(torch.bfloat16)
-                continue
-            codes, s = quantize_e4m3(x)
-            out[n] = codes
-            out["s" + n] = s
-    else:
-        raise ValueError(f"unknown dtype {dtype}")
-    return out
+    return _cast({}, ["q", "k", "v", "do"][: len(xs)], xs, dtype)
 
 
 def _cast(out, names, xs, dtype):
@@ -110,12 +115,13 @@ def _cast(out, names, xs, dtype):
         out.update(zip(names, xs))
     elif dtype == "bf16":
         out.update((n, x.to(torch.bfloat16)) for n, x in zip(names, xs))
-    elif dtype == "fp8":
+    elif dtype in ("fp8", "fp8e5m2"):
+        quant = quantize_e4m3 if dtype == "fp8" else quantize_e5m2
         for n, x in zip(names, xs):
             if n == "do":
                 out[n] = x.to(torch.bfloat16)
                 continue
-            codes, s = quantize_e4m3(x)
+            codes, s = quant(x)
             out[n] = codes
             out["s" + n] = s
     else:
@@ -144,6 +150,6 @@ def sample_rows(seed, B, H, N, size):
 
 def to_numpy(t):
     """CPU tensor -> numpy array that the oracle reads (exact for f32/bf16; uint8 codes for fp8)."""
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.view(torch.uint8).numpy()
     return t.to(torch.float32).numpy()

@@ -18,4 +18,5 @@ from .attention import (  # noqa: F401
     brute_force_forward,
     brute_force_backward,
     decode_e4m3fn,
+    decode_e5m2,
 )

@@ -56,7 +56,7 @@ __all__ = [
     "scores", "probabilities", "forward", "forward_quantized", "backward",
     "forward_gqa", "backward_gqa", "forward_decode",
     "online_softmax_chunked", "brute_force_forward", "brute_force_backward",
-    "decode_e4m3fn",
+    "decode_e4m3fn", "decode_e5m2",
 ]
 
 
@@ -145,17 +145,38 @@ def decode_e4m3fn(codes):
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
 
 
-def forward_quantized(qc, kc, vc, sq, sk, sv, scale, causal, rows=None):
-    """Attention of per-tensor-scaled FP8 E4M3 inputs.
+def decode_e5m2(codes):
+    """Decode OCP FP8 E5M2 bytes to float64.
 
-    qc, kc, vc: uint8 E4M3 codes [B,H,N,d]; sq, sk, sv: the float32
-    per-tensor scales. The inputs the path sees are code * scale, so the
-    oracle is `forward` on exactly those values (float64 holds each product
-    exactly: 4 significant bits times 24).
+    Format: 1 sign bit, 5 exponent bits with bias 15, 2 mantissa bits;
+    exponent field 0 is subnormal (mantissa * 2^-16); exponent field 31 is
+    infinity (mantissa 0) or NaN; largest finite magnitude 57344. This is
+    the E5M2 format the pages name next to E4M3 for the FP8 path
+    ([FAQ-short] answer paragraph 2; [FAQ-mcq] version table).
     """
-    q = decode_e4m3fn(qc) * float(np.float32(sq))
-    k = decode_e4m3fn(kc) * float(np.float32(sk))
-    v = decode_e4m3fn(vc) * float(np.float32(sv))
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    mant = c & 0x3
+    normal = sign * (1.0 + mant / 4.0) * np.exp2(e - 15.0)
+    sub = sign * mant * 2.0 ** -16
+    val = np.where(e == 0, sub, normal)
+    val = np.where((e == 31) & (mant == 0), sign * np.inf, val)
+    return np.where((e == 31) & (mant != 0), np.nan, val)
+
+
+def forward_quantized(qc, kc, vc, sq, sk, sv, scale, causal, rows=None, fmt="e4m3"):
+    """Attention of per-tensor-scaled FP8 inputs.
+
+    qc, kc, vc: uint8 codes [B,H,N,d] in the format `fmt` ("e4m3" or
+    "e5m2"); sq, sk, sv: the float32 per-tensor scales. The inputs the path
+    sees are code * scale, so the oracle is `forward` on exactly those values
+    (float64 holds each product exactly: at most 4 significant bits times 24).
+    """
+    dec = decode_e4m3fn if fmt == "e4m3" else decode_e5m2
+    q = dec(qc) * float(np.float32(sq))
+    k = dec(kc) * float(np.float32(sk))
+    v = dec(vc) * float(np.float32(sv))
     return forward(q, k, v, scale, causal, rows)
 
 

@@ -399,11 +399,37 @@ def pin_decode_is_tail_of_full(o):
     assert np.max(np.abs(a - b)) == 0.0 and np.max(np.abs(al - bl)) == 0.0
 
 
+def pin_e5m2_decode(o):
+    """OCP E5M2 decoding: fixed points of the format, and torch's own
+    float8_e5m2 conversion (a library implementation) on all 256 codes."""
+    import torch
+    dec = o.decode_e5m2(np.arange(256, dtype=np.uint8))
+    assert dec[0x00] == 0.0 and dec[0x3C] == 1.0 and dec[0xBC] == -1.0
+    assert dec[0x7B] == 57344.0 and dec[0x01] == 2.0 ** -16 and dec[0x04] == 2.0 ** -14
+    assert dec[0x3D] == 1.25 and dec[0x40] == 2.0 and dec[0x38] == 0.5
+    assert dec[0x7C] == np.inf and dec[0xFC] == -np.inf and math.isnan(dec[0x7D]) and math.isnan(dec[0xFF])
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    both_nan = np.isnan(dec) & np.isnan(ref)
+    assert np.all(both_nan | (dec == ref))
+
+
+def pin_quantized_forward_e5m2(o):
+    """The E5M2 entry computes attention of code * scale."""
+    g = _rng(22)
+    codes = [g.integers(0, 0x7B, size=(1, 1, 9, 4), dtype=np.uint8) | (g.integers(0, 2, size=(1, 1, 9, 4), dtype=np.uint8) << 7) for _ in range(3)]
+    sc = (0.001, 0.002, 0.003)
+    out, lse = o.forward_quantized(*codes, *sc, 0.5, True, fmt="e5m2")
+    assert o.decode_e5m2(np.uint8(0x3E)) == 1.5
+    vals = [o.decode_e5m2(cd) * float(np.float32(s)) for cd, s in zip(codes, sc)]
+    ref, ref_lse = o.forward(*vals, 0.5, True)
+    assert np.max(np.abs(out - ref)) == 0.0 and np.max(np.abs(lse - ref_lse)) == 0.0
+
+
 ALL_PINS = [
     pin_hand_example, pin_rows_sum_to_one, pin_chunked_equals_full, pin_constant_column,
     pin_uniform_scores, pin_brute_force, pin_torch_sdpa, pin_finite_differences,
     pin_single_key, pin_two_keys, pin_permutations, pin_backward_invariants,
     pin_masked_chunk, pin_sampled_rows, pin_e4m3_decode, pin_quantized_forward,
     pin_gqa_torch, pin_gqa_brute_force, pin_gqa_finite_differences, pin_decode_torch,
-    pin_decode_is_tail_of_full,
+    pin_decode_is_tail_of_full, pin_e5m2_decode, pin_quantized_forward_e5m2,
 ]

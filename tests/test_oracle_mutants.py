@@ -36,7 +36,10 @@ MUTANTS = {
     "e4m3_bias8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
     "e4m3_subnormal": ("sub = sign * mant * 2.0 ** -9", "sub = sign * mant * 2.0 ** -10"),
     "softmax_no_normalise": ("return e / l, m[:, 0], l[:, 0]", "return e, m[:, 0], l[:, 0]"),
-    "dequant_scale_dropped": ("q = decode_e4m3fn(qc) * float(np.float32(sq))", "q = decode_e4m3fn(qc)"),
+    "dequant_scale_dropped": ("q = dec(qc) * float(np.float32(sq))", "q = dec(qc)"),
+    "e5m2_bias16": ("np.exp2(e - 15.0)", "np.exp2(e - 16.0)"),
+    "e5m2_mantissa_bits3": ("(1.0 + mant / 4.0)", "(1.0 + mant / 8.0)"),
+    "e5m2_subnormal": ("sub = sign * mant * 2.0 ** -16", "sub = sign * mant * 2.0 ** -17"),
     "gqa_head_map_modulo": ("return forward(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), scale, causal, rows)",
                             "return forward(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1)), scale, causal, rows)"),
     "gqa_dk_first_head_only": ("dke.reshape(B, Hkv, G, N, d).sum(axis=2)", "dke.reshape(B, Hkv, G, N, d)[:, :, 0]"),
