@@ -53,7 +53,8 @@ typedef enum {
 typedef enum {
   FA_F32 = 0,      /* IEEE float32                                       */
   FA_BF16 = 1,     /* bfloat16                                           */
-  FA_FP8_E4M3 = 3  /* OCP FP8 E4M3 ("fn": finite only, max 448), inputs only */
+  FA_FP8_E4M3 = 3, /* OCP FP8 E4M3 ("fn": finite only, max 448), inputs only */
+  FA_FP8_E5M2 = 4  /* OCP FP8 E5M2 (max finite 57344), inputs only          */
 } fa_dtype;
 
 /*
@@ -74,9 +75,11 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
  *              FA_BF16 (bf16 operands, P rounded to bf16 for P.V),
  *              FA_FP8_E4M3 (E4M3 codes; P quantised to E4M3 for P.V; the
  *              FP8 path of the version table on the FlashAttention-family
- *              multiple-choice page).
- *   o_dtype  : FA_F32 or FA_BF16 (FA_F32 with FA_FP8_E4M3 is unsupported).
- *   descale  : FA_FP8_E4M3 only: DEVICE pointer to 3 float32 per-tensor
+ *              multiple-choice page),
+ *              FA_FP8_E5M2 (E5M2 codes, the other FP8 format the pages name
+ *              for that path; P is still quantised to E4M3).
+ *   o_dtype  : FA_F32 or FA_BF16 (FA_F32 with an FP8 input is unsupported).
+ *   descale  : FP8 inputs only: DEVICE pointer to 3 float32 per-tensor
  *              scales {s_q, s_k, s_v}; the inputs stand for code * s.
  *              Must be NULL for the other dtypes.
  * Accumulation is float32 for every dtype; the softmax runs in float32 and

@@ -22,8 +22,10 @@ FA_ERR_LAUNCH = -4
 FA_F32 = 0
 FA_BF16 = 1
 FA_FP8_E4M3 = 3
+FA_FP8_E5M2 = 4
 
-_TORCH_DTYPE = {FA_F32: torch.float32, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.float8_e4m3fn}
+_TORCH_DTYPE = {FA_F32: torch.float32, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.float8_e4m3fn,
+                FA_FP8_E5M2: torch.float8_e5m2}
 
 EXPORTS = ("fa_forward", "fa_forward_typed", "fa_backward", "fa_backward_workspace_bytes", "fa_forward_gqa",
            "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_decode_workspace_bytes", "fa_decode",

@@ -46,9 +46,10 @@ int fa_forward_gqa(int in_dtype, int o_dtype, const void* q, const void* k, cons
   int st = check_shape(B, H, N, d, scale);
   if (st != FA_OK) return st;
   if (Hkv < 1 || (H > 0 && (Hkv > H || H % Hkv != 0))) return FA_ERR_INVALID_ARG;
-  if (in_dtype != FA_F32 && in_dtype != FA_BF16 && in_dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (in_dtype != FA_F32 && in_dtype != FA_BF16 && in_dtype != FA_FP8_E4M3 && in_dtype != FA_FP8_E5M2)
+    return FA_ERR_INVALID_ARG;
   if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
-  if (in_dtype == FA_FP8_E4M3) {
+  if (in_dtype == FA_FP8_E4M3 || in_dtype == FA_FP8_E5M2) {
     if (o_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (!descale) return FA_ERR_INVALID_ARG;
   } else if (descale) {

@@ -433,8 +433,8 @@ int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, cons
   } else if (in_dtype == FA_F32) {
     err = (o_dtype == FA_BF16) ? FA_DISPATCH(launch_f32, d, causal, bf16, q, k, v, o, lse, BH, G, N, c, stream)
                                : FA_DISPATCH(launch_f32, d, causal, float, q, k, v, o, lse, BH, G, N, c, stream);
-  } else if (in_dtype == FA_FP8_E4M3 && o_dtype == FA_BF16) {
-    err = launch_forward_fp8(q, k, v, descale, o, lse, BH, G, N, d, scale, causal, stream);
+  } else if ((in_dtype == FA_FP8_E4M3 || in_dtype == FA_FP8_E5M2) && o_dtype == FA_BF16) {
+    err = launch_forward_fp8(q, k, v, descale, o, lse, BH, G, N, d, scale, causal, in_dtype == FA_FP8_E5M2, stream);
   } else {
     return FA_ERR_UNSUPPORTED;
   }

@@ -1,10 +1,12 @@
-// Forward pass with FP8 E4M3 operands (the FP8 path of the version table on
-// the FlashAttention-family multiple-choice page; E4M3 is named on the
+// Forward pass with FP8 operands (the FP8 path of the version table on the
+// FlashAttention-family multiple-choice page; E4M3 and E5M2 are named on the
 // short-answer page, answer paragraph 2).
 //
-// Inputs are E4M3 codes with per-tensor float32 scales s_q, s_k, s_v (the
+// Inputs are E4M3 or E5M2 codes (template FMT = 0 / 1, the instruction's
+// operand format fields) with per-tensor float32 scales s_q, s_k, s_v (the
 // values they stand for are code * s). Both products run on the fp8 matrix
-// cores (v_mfma_f32_32x32x64_f8f6f4, float32 accumulation):
+// cores (v_mfma_f32_32x32x64_f8f6f4, float32 accumulation); P is always
+// quantised to E4M3:
 //   S^T = K Q^T           scaled by scale * s_q * s_k * log2(e) in the exponent
 //   O^T += V^T P^T        P quantised to E4M3, O finished as acc * s_v / l
 // The online softmax is the one of the bf16 kernel (running max m, running
@@ -54,7 +56,7 @@ constexpr float kP8Shift = 5.f;
 
 // 8 waves x 32 query rows (BR = 256), blocks of BC = 128 keys, two waves per
 // SIMD; K/V tiles HBM -> LDS by DMA into a 2-stage ring.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                          const uint8_t* __restrict__ V, bf16* __restrict__ O,
                                                          float* __restrict__ LSE, const float* __restrict__ descale,
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
         const i32x4 a0 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][0]);
         const i32x4 a1 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][1]);
         const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        s[kt] = mfma_fp8(a, qf[kk], s[kt]);
+        s[kt] = mfma_f8<FMT, FMT>(a, qf[kk], s[kt]);
       }
     }
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
           a[2 * t] = r[0];
           a[2 * t + 1] = r[1];
         }
-        acc[dt] = mfma_fp8(a, pf, acc[dt]);
+        acc[dt] = mfma_f8<FMT, 0>(a, pf, acc[dt]);  // V in the input format, P in E4M3
       }
     }
   };
@@ -244,21 +246,28 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 static hipError_t launch_fp8_d(const void* q, const void* k, const void* v, const float* descale, void* o,
                                float* lse, int BH, int G, int N, float scale, hipStream_t st) {
   const int nqb = (N + 255) / 256;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(BH * nqb), dim3(512), 0, st, (const uint8_t*)q,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, FMT>), dim3(BH * nqb), dim3(512), 0, st, (const uint8_t*)q,
                      (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, descale, BH, G, N, nqb, scale);
   return hipGetLastError();
 }
 
+template <int FMT>
+static hipError_t launch_fp8_fmt(const void* q, const void* k, const void* v, const float* descale, void* o,
+                                 float* lse, int BH, int G, int N, int d, float scale, int causal, hipStream_t st) {
+  if (d == 64) return causal ? launch_fp8_d<64, true, FMT>(q, k, v, descale, o, lse, BH, G, N, scale, st)
+                             : launch_fp8_d<64, false, FMT>(q, k, v, descale, o, lse, BH, G, N, scale, st);
+  return causal ? launch_fp8_d<128, true, FMT>(q, k, v, descale, o, lse, BH, G, N, scale, st)
+                : launch_fp8_d<128, false, FMT>(q, k, v, descale, o, lse, BH, G, N, scale, st);
+}
+
 hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const float* descale, void* o, float* lse,
-                              int BH, int G, int N, int d, float scale, int causal, hipStream_t st) {
-  if (d == 64) return causal ? launch_fp8_d<64, true>(q, k, v, descale, o, lse, BH, G, N, scale, st)
-                             : launch_fp8_d<64, false>(q, k, v, descale, o, lse, BH, G, N, scale, st);
-  return causal ? launch_fp8_d<128, true>(q, k, v, descale, o, lse, BH, G, N, scale, st)
-                : launch_fp8_d<128, false>(q, k, v, descale, o, lse, BH, G, N, scale, st);
+                              int BH, int G, int N, int d, float scale, int causal, int e5m2, hipStream_t st) {
+  return e5m2 ? launch_fp8_fmt<1>(q, k, v, descale, o, lse, BH, G, N, d, scale, causal, st)
+              : launch_fp8_fmt<0>(q, k, v, descale, o, lse, BH, G, N, d, scale, causal, st);
 }
 
 }  // namespace fa

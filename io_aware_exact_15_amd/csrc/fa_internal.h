@@ -13,10 +13,10 @@ int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, cons
                    const float* descale, void* o, float* lse, int B, int H, int Hkv, int N, int d,
                    float scale, int causal, hipStream_t stream);
 
-// FP8 E4M3 forward launch (descale: device pointer to {s_q, s_k, s_v});
-// G = query heads per key/value head.
+// FP8 forward launch (descale: device pointer to {s_q, s_k, s_v}); inputs
+// E4M3 (e5m2 = 0) or E5M2 (e5m2 = 1); G = query heads per key/value head.
 hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const float* descale, void* o, float* lse,
-                              int BH, int G, int N, int d, float scale, int causal, hipStream_t stream);
+                              int BH, int G, int N, int d, float scale, int causal, int e5m2, hipStream_t stream);
 
 // Backward launch; arguments already validated by the ABI layer. `workspace`
 // holds at least backward_workspace_bytes(B*H*N, B*Hkv*N, d) bytes.

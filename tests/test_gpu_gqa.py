@@ -22,7 +22,7 @@ def gpu_forward_gqa(inp, dtype, causal, o_dtype="bf16"):
     o = torch.empty(B, H, N, d, dtype=torch.bfloat16 if o_dtype == "bf16" else torch.float32, device=dev)
     lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
     descale = None
-    if dtype == "fp8":
+    if dtype in ("fp8", "fp8e5m2"):
         descale = torch.tensor([inp["sq"], inp["sk"], inp["sv"]], dtype=torch.float32, device=dev)
     fa.fa_forward_gqa(FA_DT[dtype], FA_DT[o_dtype], qd, kd, vd, descale, o, lse, scale, causal)
     torch.cuda.synchronize()
@@ -30,8 +30,9 @@ def gpu_forward_gqa(inp, dtype, causal, o_dtype="bf16"):
 
 
 def _values(inp, dtype):
-    if dtype == "fp8":
-        return [oracle.decode_e4m3fn(inputs.to_numpy(inp[n])) * float(np.float32(inp["s" + n])) for n in "qkv"]
+    if dtype in ("fp8", "fp8e5m2"):
+        dec = oracle.decode_e4m3fn if dtype == "fp8" else oracle.decode_e5m2
+        return [dec(inputs.to_numpy(inp[n])) * float(np.float32(inp["s" + n])) for n in "qkv"]
     return [inputs.to_numpy(inp[n]) for n in "qkv"]
 
 
@@ -43,7 +44,7 @@ def _check_fwd(B, H, Hkv, N, d, seed, dtype, causal, o_dtype="bf16", sample=None
     ro, rl = oracle.forward_gqa(*_values(inp, dtype), 1.0 / math.sqrt(d), causal, rows)
     if rows is not None:
         o, lse = gather_rows(o, rows), gather_rows(lse, rows)
-    tol_dtype = "f32" if (dtype == "f32" and o_dtype == "f32") else ("fp8" if dtype == "fp8" else "bf16")
+    tol_dtype = "f32" if (dtype == "f32" and o_dtype == "f32") else ("fp8" if dtype.startswith("fp8") else "bf16")
     mx, rms = assert_close(o, ro, tol_dtype, "O", o_bf16=(o_dtype == "bf16"))
     lmx = assert_lse(lse, rl, "lse")
     print(f"  O max={mx:.3g} rms={rms:.3g} lse={lmx:.3g}", flush=True)
@@ -80,6 +81,12 @@ def test_fwd_edge_f32(shape, causal):
 def test_fwd_edge_fp8(shape):
     B, H, Hkv, N, d = shape
     _check_fwd(B, H, Hkv, N, d, 800 + N, "fp8", True)
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 300, 128), (1, 4, 1, 129, 64)], ids=["kv2", "mqa"])
+def test_fwd_edge_fp8_e5m2(shape):
+    B, H, Hkv, N, d = shape
+    _check_fwd(B, H, Hkv, N, d, 850 + N, "fp8e5m2", True)
 
 
 def test_fwd_gqa_equals_repeated_heads():
