@@ -82,6 +82,12 @@ def quantize_e5m2(x):
     return codes, np.float32(scale.item())
 
 
+# FP8 backward: the 4K backward shape with E4M3 Q, K, V and an E5M2 dO.
+FP8_BWD_WORKLOADS = {
+    "bwd_fp8_causal_b2h16_n4096_d128": dict(seed=11, B=2, H=16, Hkv=16, N=4096, d=128, dtype="fp8bwd",
+                                            causal=(True,), sample=None, backward=True),
+}
+
 # FP8 E5M2 variant of the 64K FP8 workload.
 FP8_E5M2_WORKLOADS = {
     "fwd_fp8e5m2_causal_b1h8_n65536_d128": dict(seed=10, B=1, H=8, N=65536, d=128, dtype="fp8e5m2",
@@ -122,6 +128,11 @@ def _cast(out, names, xs, dtype):
                 out[n] = x.to(torch.bfloat16)
                 continue
             codes, s = quant(x)
+            out[n] = codes
+            out["s" + n] = s
+    elif dtype == "fp8bwd":  # E4M3 Q, K, V and an E5M2 gradient dO, per-tensor scales
+        for n, x in zip(names, xs):
+            codes, s = (quantize_e5m2 if n == "do" else quantize_e4m3)(x)
             out[n] = codes
             out["s" + n] = s
     else:

@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     forward_gqa,
     backward_gqa,
     forward_decode,
+    backward_quantized,
     online_softmax_chunked,
     brute_force_forward,
     brute_force_backward,

@@ -54,7 +54,7 @@ import numpy as np
 
 __all__ = [
     "scores", "probabilities", "forward", "forward_quantized", "backward",
-    "forward_gqa", "backward_gqa", "forward_decode",
+    "forward_gqa", "backward_gqa", "forward_decode", "backward_quantized",
     "online_softmax_chunked", "brute_force_forward", "brute_force_backward",
     "decode_e4m3fn", "decode_e5m2",
 ]
@@ -279,6 +279,24 @@ def forward_decode(q, k, v, scale, causal):
             out[b, h] = p @ v[b, h // G]
             lse[b, h] = m + np.log(l)
     return out, lse
+
+
+def backward_quantized(qc, kc, vc, doc, sq, sk, sv, sdo, scale, causal, fmt_in="e4m3", fmt_do="e5m2"):
+    """Gradients of <O, dO> for per-tensor-scaled FP8 inputs and gradient.
+
+    qc, kc, vc: uint8 codes [B,H(kv),N,d] in `fmt_in`; doc: uint8 codes of dO
+    in `fmt_do` (E5M2, the wider-range FP8 format the pages name next to
+    E4M3, for the gradient); sq, sk, sv, sdo: float32 scales. The values are
+    code * scale (exact in float64), and the gradients are those of
+    `backward_gqa` on exactly those values.
+    """
+    dec_in = decode_e4m3fn if fmt_in == "e4m3" else decode_e5m2
+    dec_do = decode_e4m3fn if fmt_do == "e4m3" else decode_e5m2
+    q = dec_in(qc) * float(np.float32(sq))
+    k = dec_in(kc) * float(np.float32(sk))
+    v = dec_in(vc) * float(np.float32(sv))
+    do = dec_do(doc) * float(np.float32(sdo))
+    return backward_gqa(q, k, v, do, scale, causal)
 
 
 def online_softmax_chunked(s_row, v_rows, bounds):

@@ -425,11 +425,30 @@ def pin_quantized_forward_e5m2(o):
     assert np.max(np.abs(out - ref)) == 0.0 and np.max(np.abs(lse - ref_lse)) == 0.0
 
 
+def pin_quantized_backward(o):
+    """The FP8 backward entry is the backward of code * scale (E4M3 inputs,
+    E5M2 gradient), including shared key/value heads."""
+    g = _rng(23)
+    rnd = lambda shape, top: g.integers(0, top, size=shape, dtype=np.uint8) | (g.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+    qc, kc, vc = rnd((1, 4, 7, 4), 0x7E), rnd((1, 2, 7, 4), 0x7E), rnd((1, 2, 7, 4), 0x7E)
+    doc = rnd((1, 4, 7, 4), 0x7B)
+    sc = (0.01, 0.02, 0.03, 0.0004)
+    got = o.backward_quantized(qc, kc, vc, doc, *sc, 0.5, True)
+    q = o.decode_e4m3fn(qc) * float(np.float32(sc[0]))
+    k = o.decode_e4m3fn(kc) * float(np.float32(sc[1]))
+    v = o.decode_e4m3fn(vc) * float(np.float32(sc[2]))
+    do = o.decode_e5m2(doc) * float(np.float32(sc[3]))
+    ref = o.backward_gqa(q, k, v, do, 0.5, True)
+    for a, b in zip(got, ref):
+        assert np.max(np.abs(a - b)) == 0.0
+    assert o.decode_e5m2(np.uint8(0x3F)) == 1.75
+
+
 ALL_PINS = [
     pin_hand_example, pin_rows_sum_to_one, pin_chunked_equals_full, pin_constant_column,
     pin_uniform_scores, pin_brute_force, pin_torch_sdpa, pin_finite_differences,
     pin_single_key, pin_two_keys, pin_permutations, pin_backward_invariants,
     pin_masked_chunk, pin_sampled_rows, pin_e4m3_decode, pin_quantized_forward,
     pin_gqa_torch, pin_gqa_brute_force, pin_gqa_finite_differences, pin_decode_torch,
-    pin_decode_is_tail_of_full, pin_e5m2_decode, pin_quantized_forward_e5m2,
+    pin_decode_is_tail_of_full, pin_e5m2_decode, pin_quantized_forward_e5m2, pin_quantized_backward,
 ]

@@ -37,6 +37,7 @@ MUTANTS = {
     "e4m3_subnormal": ("sub = sign * mant * 2.0 ** -9", "sub = sign * mant * 2.0 ** -10"),
     "softmax_no_normalise": ("return e / l, m[:, 0], l[:, 0]", "return e, m[:, 0], l[:, 0]"),
     "dequant_scale_dropped": ("q = dec(qc) * float(np.float32(sq))", "q = dec(qc)"),
+    "quantized_bwd_do_scale_dropped": ("do = dec_do(doc) * float(np.float32(sdo))", "do = dec_do(doc)"),
     "e5m2_bias16": ("np.exp2(e - 15.0)", "np.exp2(e - 16.0)"),
     "e5m2_mantissa_bits3": ("(1.0 + mant / 4.0)", "(1.0 + mant / 8.0)"),
     "e5m2_subnormal": ("sub = sign * mant * 2.0 ** -16", "sub = sign * mant * 2.0 ** -17"),
