@@ -166,6 +166,40 @@ def run_configs(iters=20, warmup=3):
                                   "frac_of_peak": (f + bf) / ((med + bmed) * 1e-3) / 1e12 / peak}), flush=True)
 
 
+def run_fp8_bwd_configs(iters=20, warmup=3):
+    """Times the FP8 backward workloads (E4M3 Q, K, V; E5M2 dO). The forward
+    that feeds them runs in float32 on the dequantised values (untimed)."""
+    import numpy as np
+    import torch
+
+    from io_aware_exact_15_amd import binding as fa
+    from io_aware_exact_15_amd import inputs
+
+    dev = torch.device("cuda:0")
+    for name, w in inputs.FP8_BWD_WORKLOADS.items():
+        B, H, Hkv, N, d = w["B"], w["H"], w["Hkv"], w["N"], w["d"]
+        scale = 1.0 / math.sqrt(d)
+        inp = inputs.make_inputs(B, H, N, d, w["seed"], "fp8bwd", with_do=True)
+        codes = {n: inp[n].to(dev) for n in ("q", "k", "v", "do")}
+        deq = {n: (inp[n].to(torch.float32) * float(inp["s" + n])).to(dev) for n in ("q", "k", "v")}
+        desc = torch.tensor([inp["sq"], inp["sk"], inp["sv"], inp["sdo"]], dtype=torch.float32, device=dev)
+        o = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+        for causal in w["causal"]:
+            fa.fa_forward_gqa(fa.FA_F32, fa.FA_F32, deq["q"], deq["k"], deq["v"], None, o, lse, scale, causal)
+            dq = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+            dk, dv = (torch.empty(B, Hkv, N, d, dtype=torch.float32, device=dev) for _ in range(2))
+            ws = torch.empty(fa.fa_backward_gqa_workspace_bytes(B, H, Hkv, N, d), dtype=torch.uint8, device=dev)
+            fn = lambda: fa.fa_backward_typed(fa.FA_FP8_E4M3, fa.FA_FP8_E5M2, codes["q"], codes["k"], codes["v"],
+                                              codes["do"], desc, o, fa.FA_F32, lse, dq, dk, dv, ws, scale, causal)
+            med, mn = _median_ms(torch, fn, iters, warmup)
+            bf = _flops(B, H, N, d, causal, "bwd")
+            print(json.dumps({"workload": name, "pass": "bwd", "causal": causal, "dtype": "fp8 e4m3 / e5m2 dO",
+                              "ms_median": med, "ms_min": mn, "tflops": bf / (med * 1e-3) / 1e12,
+                              "frac_of_peak": bf / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                              "peak_tflops": PEAK_BF16_TFLOPS, "note": "fp16 matrix-core operands"}), flush=True)
+
+
 def run_decode_configs(iters=20, warmup=3):
     """Times the decode workloads (HBM-bound: reported as GB/s of the
     algorithmic bytes, the K/V cache read once plus Q, O and lse)."""
@@ -210,6 +244,7 @@ def main():
 
     if args.configs:
         run_configs()
+        run_fp8_bwd_configs()
         run_decode_configs()
         return
 

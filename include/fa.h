@@ -159,6 +159,29 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
                     float scale, int causal, void* stream);
 
 /*
+ * fa_backward_typed -- backward with a choice of operand formats: bf16 Q, K,
+ * V and dO (as fa_backward_gqa), or FP8 ones: Q, K, V in in_dtype
+ * (FA_FP8_E4M3 or FA_FP8_E5M2) and dO in do_dtype (FA_FP8_E5M2, the format
+ * with the wider range, is the natural one for a gradient; FA_FP8_E4M3 is
+ * accepted). This extends the FP8 path of the version table on the
+ * FlashAttention-family multiple-choice page to the backward pass.
+ *   descale : FP8 only: DEVICE pointer to 4 float32 per-tensor scales
+ *             {s_q, s_k, s_v, s_dO}; the tensors stand for code * s. Must be
+ *             NULL for bf16.
+ * The FP8 codes are converted exactly to fp16 matrix-core operands (every
+ * E4M3 and E5M2 value is an fp16 value) and the scales are applied in
+ * float32: to the score exponent, to dP, and to dQ, dK, dV. Mixing bf16 and
+ * FP8 between the two dtypes returns FA_ERR_UNSUPPORTED. o, lse, dq, dk, dv,
+ * the workspace (fa_backward_gqa_workspace_bytes) and every other rule are
+ * those of fa_backward_gqa.
+ */
+int fa_backward_typed(int in_dtype, int do_dtype, const void* q, const void* k, const void* v,
+                      const void* dO, const float* descale, const void* o, int o_dtype,
+                      const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                      size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
+                      int causal, void* stream);
+
+/*
  * fa_decode_workspace_bytes -- workspace of fa_decode: per split of the keys
  * and per wave, an unnormalised 32 x d float32 partial output and its running
  * max and denominator; 0 for invalid sizes (see fa_decode).

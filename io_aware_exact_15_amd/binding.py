@@ -28,7 +28,8 @@ _TORCH_DTYPE = {FA_F32: torch.float32, FA_BF16: torch.bfloat16, FA_FP8_E4M3: tor
                 FA_FP8_E5M2: torch.float8_e5m2}
 
 EXPORTS = ("fa_forward", "fa_forward_typed", "fa_backward", "fa_backward_workspace_bytes", "fa_forward_gqa",
-           "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_decode_workspace_bytes", "fa_decode",
+           "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_backward_typed", "fa_decode_workspace_bytes",
+           "fa_decode",
            "fa_status_string")
 
 
@@ -60,6 +61,9 @@ def lib():
         L.fa_backward_gqa.restype = i
         L.fa_backward_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_backward_gqa_workspace_bytes.restype = sz
+        L.fa_backward_typed.argtypes = [i, i, vp, vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i,
+                                        vp]
+        L.fa_backward_typed.restype = i
         L.fa_decode.argtypes = [vp, vp, vp, vp, i, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
         L.fa_decode.restype = i
         L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -148,6 +152,18 @@ def fa_backward_gqa(q, k, v, o, o_dtype, do, lse, dq, dk, dv, workspace, scale, 
     _check(lib().fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype), _ptr(do), _ptr(lse),
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, Hkv, N, d,
                                  float(scale), int(bool(causal)), _stream(stream)), "fa_backward_gqa")
+
+
+def fa_backward_typed(in_dtype, do_dtype, q, k, v, do, descale, o, o_dtype, lse, dq, dk, dv, workspace, scale, causal,
+                      stream=None):
+    """Backward with bf16 or FP8 operands (descale: device float32[4] {s_q, s_k, s_v, s_dO} for FP8)."""
+    B, H, N, d = _dims(q)
+    Hkv = _dims(k)[1]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_backward_typed(int(in_dtype), int(do_dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(descale),
+                                   _ptr(o), int(o_dtype), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                   nbytes, B, H, Hkv, N, d, float(scale), int(bool(causal)), _stream(stream)),
+           "fa_backward_typed")
 
 
 def fa_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d):

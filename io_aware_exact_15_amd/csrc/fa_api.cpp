@@ -84,13 +84,19 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   return fa_backward_gqa_workspace_bytes(B, H, H, N, d);
 }
 
-int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
-                    const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
-                    int B, int H, int Hkv, int N, int d, float scale, int causal, void* stream) {
+int fa_backward_typed(int in_dtype, int do_dtype, const void* q, const void* k, const void* v, const void* dO,
+                      const float* descale, const void* o, int o_dtype, const float* lse, float* dq, float* dk,
+                      float* dv, void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d,
+                      float scale, int causal, void* stream) {
   int st = check_shape(B, H, N, d, scale);
   if (st != FA_OK) return st;
   if (Hkv < 1 || (H > 0 && (Hkv > H || H % Hkv != 0))) return FA_ERR_INVALID_ARG;
   if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  auto fmt = [](int t) { return t == FA_BF16 ? 0 : t == FA_FP8_E4M3 ? 1 : t == FA_FP8_E5M2 ? 2 : -1; };
+  const int fin = fmt(in_dtype), fdo = fmt(do_dtype);
+  if (fin < 0 || fdo < 0) return FA_ERR_INVALID_ARG;
+  if ((fin == 0) != (fdo == 0)) return FA_ERR_UNSUPPORTED;  // both bf16 or both FP8
+  if ((fin != 0) != (descale != nullptr)) return FA_ERR_INVALID_ARG;
   if ((long long)B * H == 0) return FA_OK;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
@@ -99,7 +105,14 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
   if (!workspace || workspace_bytes < fa_backward_gqa_workspace_bytes(B, H, Hkv, N, d) || !aligned16(workspace))
     return FA_ERR_WORKSPACE;
   return fa::launch_backward(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, B, H, Hkv, N, d, scale, causal,
-                             (hipStream_t)stream);
+                             fin, fdo, descale, (hipStream_t)stream);
+}
+
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
+                    const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                    int B, int H, int Hkv, int N, int d, float scale, int causal, void* stream) {
+  return fa_backward_typed(FA_BF16, FA_BF16, q, k, v, dO, nullptr, o, o_dtype, lse, dq, dk, dv, workspace,
+                           workspace_bytes, B, H, Hkv, N, d, scale, causal, stream);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,

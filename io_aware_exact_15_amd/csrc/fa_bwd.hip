@@ -124,13 +124,45 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(i32x4 raw, float* f) {
 }
 
 // ---------------------------------------------------------------------------
-// Per row: fp16 copies, D_i = sum_t dO_it * O_it, NL_i = -lse_i * log2(e).
-// One group of D/8 lanes per row, 16 bytes of each input per lane.
-template <int D, typename OT>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                                                       const bf16* __restrict__ V, const bf16* __restrict__ dO,
+// 8 FP8 codes (raw 8 bytes; E4M3 if E5M2 == false) -> 8 fp16 (exact: every
+// E4M3 and E5M2 value is an fp16 value); f gets the float values.
+template <bool E5M2, int SEL>
+__device__ __forceinline__ float fp8_byte(int w) {
+  return E5M2 ? __builtin_amdgcn_cvt_f32_bf8(w, SEL) : __builtin_amdgcn_cvt_f32_fp8(w, SEL);
+}
+template <bool E5M2>
+__device__ __forceinline__ f16x8 fp8x8_to_f16(i32x2 raw, float* f) {
+  f[0] = fp8_byte<E5M2, 0>(raw[0]);
+  f[1] = fp8_byte<E5M2, 1>(raw[0]);
+  f[2] = fp8_byte<E5M2, 2>(raw[0]);
+  f[3] = fp8_byte<E5M2, 3>(raw[0]);
+  f[4] = fp8_byte<E5M2, 0>(raw[1]);
+  f[5] = fp8_byte<E5M2, 1>(raw[1]);
+  f[6] = fp8_byte<E5M2, 2>(raw[1]);
+  f[7] = fp8_byte<E5M2, 3>(raw[1]);
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (f16)f[j];
+  return r;
+}
+
+// Element format of a backward input: 0 = bf16, 1 = FP8 E4M3, 2 = FP8 E5M2.
+template <int FMT>
+__device__ __forceinline__ f16x8 load8_f16(const void* base, size_t elem, float* f) {
+  if (FMT == 0) return bf16x8_to_f16(*(const i32x4*)((const bf16*)base + elem), f);
+  return fp8x8_to_f16<FMT == 2>(*(const i32x2*)((const uint8_t*)base + elem), f);
+}
+
+// Per row: fp16 copies of the operands (FP8 codes are copied as their code
+// values; the per-tensor scales are applied by the kernels that use them),
+// D_i = sum_t dO_it * O_it (with dO's scale), NL_i = -lse_i * log2(e).
+// One group of D/8 lanes per row, 8 elements of each input per lane.
+template <int D, typename OT, int FIN, int FDO>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ Q, const void* __restrict__ K,
+                                                       const void* __restrict__ V, const void* __restrict__ dO,
                                                        const OT* __restrict__ O, const float* __restrict__ LSE,
-                                                       BwdWs ws, long rows, long kv_rows) {
+                                                       const float* __restrict__ desc, BwdWs ws, long rows,
+                                                       long kv_rows) {
   constexpr int L = D / 8;
   const long t = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = t / L;
@@ -139,12 +171,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
   if (row < rows) {
     const size_t off = (size_t)row * D + 8 * part;
     float tmp[8], dof[8];
-    *(f16x8*)(ws.q + off) = bf16x8_to_f16(*(const i32x4*)(Q + off), tmp);
+    *(f16x8*)(ws.q + off) = load8_f16<FIN>(Q, off, tmp);
     if (row < kv_rows) {  // key/value heads: kv_rows <= rows
-      *(f16x8*)(ws.k + off) = bf16x8_to_f16(*(const i32x4*)(K + off), tmp);
-      *(f16x8*)(ws.v + off) = bf16x8_to_f16(*(const i32x4*)(V + off), tmp);
+      *(f16x8*)(ws.k + off) = load8_f16<FIN>(K, off, tmp);
+      *(f16x8*)(ws.v + off) = load8_f16<FIN>(V, off, tmp);
     }
-    *(f16x8*)(ws.dO + off) = bf16x8_to_f16(*(const i32x4*)(dO + off), dof);
+    *(f16x8*)(ws.dO + off) = load8_f16<FDO>(dO, off, dof);
     const OT* o = O + off;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc += dof[j] * (float)o[j];
@@ -152,7 +184,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
 #pragma unroll
   for (int s = L / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (row < rows && part == 0) {
-    ws.Dv[row] = acc;
+    ws.Dv[row] = FDO == 0 ? acc : acc * desc[3];
     ws.NL[row] = -LSE[row] * kLog2e;
   }
 }
@@ -166,9 +198,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
 // dP = dO V^T. The two partial sums of a key group are added through LDS at
 // the end. With grouped heads the workgroup belongs to one query head and
 // reads its key/value head's K and V.
-template <int D, bool CAUSAL>
+// SCALED: the operands are FP8 codes with per-tensor scales desc = {s_q, s_k,
+// s_v, s_dO}: S gets s_q s_k (folded into the exponent), dP gets s_dO s_v,
+// dV s_dO and dK s_q.
+template <int D, bool CAUSAL, bool SCALED>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __restrict__ dK, float* __restrict__ dV,
-                                                          int BH, int G, int N, int nkb, float c, float scale) {
+                                                          int BH, int G, int N, int nkb, float c, float scale,
+                                                          const float* __restrict__ desc) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int ROWB = 2 * D, TILEB = BQ * ROWB, CPR = D / 8;
   constexpr int VTB = BKV * ROWB;           // resident K (and V) tile bytes
@@ -183,6 +219,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
   __shared__ __attribute__((aligned(1024))) char lds_v[VTB];
   __shared__ __attribute__((aligned(1024))) char lds[NST][STB];
 
+  float cS = c, sPV = 1.f, fK = scale, fV = 1.f;
+  if (SCALED) {
+    cS = c * desc[0] * desc[1];
+    sPV = desc[3] * desc[2];
+    fK = scale * desc[0];
+    fV = desc[3];
+  }
   int bh, kb;
   map_head_block(blockIdx.x, BH, G, nkb, CAUSAL, bh, kb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -296,10 +339,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
       const f32x4 d4 = *(const f32x4*)(dd + 8 * g + 4 * hi);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[4 * g + r], c, l4[r]));
+        float p = fast_exp2(__builtin_fmaf(s[4 * g + r], cS, l4[r]));
         if (masked && key > q0 + 8 * g + 4 * hi + r) p = 0.f;
         pv[4 * g + r] = p;
-        dsv[4 * g + r] = p * (dp[4 * g + r] - d4[r]);
+        dsv[4 * g + r] = p * ((SCALED ? dp[4 * g + r] * sPV : dp[4 * g + r]) - d4[r]);
       }
     }
     f16x8 pf[2], df[2];
@@ -377,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
     __syncthreads();
     if (qh == 0) {
       float* out = pass == 0 ? dK : dV;
-      const float f = pass == 0 ? scale : 1.f;
+      const float f = pass == 0 ? fK : fV;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -393,9 +436,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
 
 // ---------------------------------------------------------------------------
 // dQ. 8 waves x 32 queries (BR = 256), two waves per SIMD; key blocks of 64.
-template <int D, bool CAUSAL>
+// SCALED as for bwd_dkdv: S gets s_q s_k, dP gets s_dO s_v, dQ gets s_k.
+template <int D, bool CAUSAL, bool SCALED>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restrict__ dQ, int BH, int G, int N, int nqb,
-                                                        float c, float scale) {
+                                                        float c, float scale, const float* __restrict__ desc) {
   constexpr int NW = 8, BR = 32 * NW, BC = 64;
   constexpr int ROWB = 2 * D, TILEB = BC * ROWB, CPR = D / 8;
   constexpr int NPW = CPR * BC / 64 / NW;
@@ -403,6 +447,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
   static_assert(NPW >= 1, "tile split");
   __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
 
+  float cS = c, sPV = 1.f, fQ = scale;
+  if (SCALED) {
+    cS = c * desc[0] * desc[1];
+    sPV = desc[3] * desc[2];
+    fQ = scale * desc[1];
+  }
   int bh, qb;
   map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,9 +560,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
       const int lim = min(CAUSAL ? q : N - 1, N - 1) - (k0 + 32 * kt) - 4 * hi;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(s[kt][i], c, nl));
+        float p = fast_exp2(__builtin_fmaf(s[kt][i], cS, nl));
         if (need_mask && 8 * (i / 4) + (i % 4) > lim) p = 0.f;
-        dsv[i] = p * (dp[kt][i] - dq_d);
+        dsv[i] = p * ((SCALED ? dp[kt][i] * sPV : dp[kt][i]) - dq_d);
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
@@ -562,8 +612,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 v = {acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale, acc[dt][4 * g + 2] * scale,
-                   acc[dt][4 * g + 3] * scale};
+        f32x4 v = {acc[dt][4 * g] * fQ, acc[dt][4 * g + 1] * fQ, acc[dt][4 * g + 2] * fQ,
+                   acc[dt][4 * g + 3] * fQ};
         *(f32x4*)(dst + 32 * dt + 8 * g) = v;
       }
   }
@@ -584,28 +634,44 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restr
   *(f32x4*)(out + e) = acc;
 }
 
-template <int D, bool CAUSAL>
+template <int D, typename OT, int FIN, int FDO>
+static void launch_prep(const void* q, const void* k, const void* v, const void* dO, const void* o, const float* lse,
+                        const float* desc, const BwdWs& ws, long rows, long kv_rows, hipStream_t st) {
+  const long threads = rows * (D / 8);
+  const int blocks = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL((bwd_prep_kernel<D, OT, FIN, FDO>), dim3(blocks), dim3(256), 0, st, q, k, v, dO, (const OT*)o,
+                     lse, desc, ws, rows, kv_rows);
+}
+
+template <int D, typename OT>
+static void launch_prep_fmt(int fin, int fdo, const void* q, const void* k, const void* v, const void* dO,
+                            const void* o, const float* lse, const float* desc, const BwdWs& ws, long rows,
+                            long kv_rows, hipStream_t st) {
+  if (fin == 0) launch_prep<D, OT, 0, 0>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  else if (fin == 1 && fdo == 2) launch_prep<D, OT, 1, 2>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  else if (fin == 1) launch_prep<D, OT, 1, 1>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  else if (fdo == 2) launch_prep<D, OT, 2, 2>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  else launch_prep<D, OT, 2, 1>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+}
+
+template <int D, bool CAUSAL, bool SCALED>
 static hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
                                const float* lse, float* dq, float* dk, float* dv, void* workspace, int BH, int G,
-                               int N, float scale, hipStream_t st) {
+                               int N, float scale, int fin, int fdo, const float* desc, hipStream_t st) {
   const long rows = (long)BH * N, kv_rows = rows / G;
   const BwdWs ws = carve_ws(workspace, (size_t)rows, (size_t)kv_rows, D);
-  const long threads = rows * (D / 8);
-  const int pre_blocks = (int)((threads + 255) / 256);
   if (o_dtype == FA_F32)
-    hipLaunchKernelGGL((bwd_prep_kernel<D, float>), dim3(pre_blocks), dim3(256), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, (const float*)o, lse, ws, rows, kv_rows);
+    launch_prep_fmt<D, float>(fin, fdo, q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
   else
-    hipLaunchKernelGGL((bwd_prep_kernel<D, bf16>), dim3(pre_blocks), dim3(256), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, (const bf16*)o, lse, ws, rows, kv_rows);
+    launch_prep_fmt<D, bf16>(fin, fdo, q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float c = scale * kLog2e;
   const int nkb = (N + 127) / 128;
   float* dk_out = G > 1 ? ws.dKp : dk;  // grouped heads: per-query-head results, summed below
   float* dv_out = G > 1 ? ws.dVp : dv;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(BH * nkb), dim3(512), 0, st, ws, dk_out, dv_out, BH, G, N,
-                     nkb, c, scale);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SCALED>), dim3(BH * nkb), dim3(512), 0, st, ws, dk_out, dv_out, BH,
+                     G, N, nkb, c, scale, desc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (G > 1) {
@@ -617,23 +683,39 @@ static hipError_t launch_bwd_d(const void* q, const void* k, const void* v, cons
     if (e != hipSuccess) return e;
   }
   const int nqb = (N + 255) / 256;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(BH * nqb), dim3(512), 0, st, ws, dq, BH, G, N, nqb, c,
-                     scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SCALED>), dim3(BH * nqb), dim3(512), 0, st, ws, dq, BH, G, N, nqb, c,
+                     scale, desc);
   return hipGetLastError();
 }
 
+template <bool SCALED>
+static hipError_t launch_bwd_s(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
+                               const float* lse, float* dq, float* dk, float* dv, void* workspace, int BH, int G,
+                               int N, int d, float scale, int causal, int fin, int fdo, const float* desc,
+                               hipStream_t st) {
+  if (d == 64)
+    return causal ? launch_bwd_d<64, true, SCALED>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N,
+                                                    scale, fin, fdo, desc, st)
+                  : launch_bwd_d<64, false, SCALED>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N,
+                                                     scale, fin, fdo, desc, st);
+  return causal ? launch_bwd_d<128, true, SCALED>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N,
+                                                   scale, fin, fdo, desc, st)
+                : launch_bwd_d<128, false, SCALED>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N,
+                                                    scale, fin, fdo, desc, st);
+}
+
+// in_fmt / do_fmt: 0 = bf16, 1 = FP8 E4M3, 2 = FP8 E5M2 (both bf16 or both
+// FP8; desc = {s_q, s_k, s_v, s_dO} for FP8, else unused).
 int launch_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype, const void* dO,
                     const float* lse, float* dq, float* dk, float* dv, void* workspace, int B, int H, int Hkv,
-                    int N, int d, float scale, int causal, hipStream_t stream) {
+                    int N, int d, float scale, int causal, int in_fmt, int do_fmt, const float* desc,
+                    hipStream_t stream) {
   const int BH = B * H, G = H / Hkv;
-  hipError_t e;
-  if (d == 64)
-    e = causal ? launch_bwd_d<64, true>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale, stream)
-               : launch_bwd_d<64, false>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale, stream);
-  else
-    e = causal ? launch_bwd_d<128, true>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale, stream)
-               : launch_bwd_d<128, false>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, scale,
-                                          stream);
+  const hipError_t e =
+      in_fmt == 0 ? launch_bwd_s<false>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, d, scale, causal,
+                                        0, 0, nullptr, stream)
+                  : launch_bwd_s<true>(q, k, v, o, o_dtype, dO, lse, dq, dk, dv, workspace, BH, G, N, d, scale, causal,
+                                       in_fmt, do_fmt, desc, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -20,10 +20,13 @@ hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const
 
 // Backward launch; arguments already validated by the ABI layer. `workspace`
 // holds at least backward_workspace_bytes(B*H*N, B*Hkv*N, d) bytes.
+// in_fmt / do_fmt: element format of Q, K, V / of dO: 0 = bf16, 1 = FP8
+// E4M3, 2 = FP8 E5M2 (both 0 or both FP8); desc = device {s_q, s_k, s_v,
+// s_dO} for FP8, unused for bf16.
 int launch_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                     const void* dO, const float* lse, float* dq, float* dk, float* dv,
                     void* workspace, int B, int H, int Hkv, int N, int d, float scale, int causal,
-                    hipStream_t stream);
+                    int in_fmt, int do_fmt, const float* desc, hipStream_t stream);
 
 // Backward workspace: D and -lse*log2(e) (float32 per query row), fp16
 // copies of Q and dO (per query row) and of K and V (per key/value row),

@@ -184,3 +184,29 @@ def test_decode_workspace_size():
     assert fa.fa_decode_workspace_bytes(1, 8, 2, 1, 100, 128) > 0
     assert fa.fa_decode_workspace_bytes(1, 8, 3, 1, 100, 128) == 0
     assert fa.fa_decode_workspace_bytes(1, 8, 2, 5, 4, 128) == 0
+
+
+def _bwd_typed(**kw):
+    a = dict(in_dtype=fa.FA_FP8_E4M3, do_dtype=fa.FA_FP8_E5M2, q=16, k=16, v=16, do=16, desc=16, o=16,
+             o_dtype=fa.FA_F32, lse=16, dq=16, dk=16, dv=16, ws=16, B=1, H=4, Hkv=2, N=40, d=128, scale=0.1,
+             causal=1)
+    a.update(kw)
+    need = fa.fa_backward_gqa_workspace_bytes(a["B"], a["H"], a["Hkv"], a["N"], a["d"])
+    return fa.lib().fa_backward_typed(a["in_dtype"], a["do_dtype"], a["q"], a["k"], a["v"], a["do"], a["desc"],
+                                      a["o"], a["o_dtype"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                                      kw.get("ws_bytes", need), a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                                      ctypes.c_float(a["scale"]), a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(desc=None), fa.FA_ERR_INVALID_ARG),                       # FP8 needs the scales
+    (dict(in_dtype=fa.FA_BF16, do_dtype=fa.FA_BF16), fa.FA_ERR_INVALID_ARG),  # bf16 must not pass scales
+    (dict(do_dtype=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED),             # mixed bf16 / FP8
+    (dict(in_dtype=fa.FA_F32), fa.FA_ERR_INVALID_ARG),
+    (dict(do_dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=8), fa.FA_ERR_WORKSPACE),
+    (dict(B=0, q=None), fa.FA_OK),
+])
+def test_backward_typed_validation(kw, status):
+    assert _bwd_typed(**kw) == status
