@@ -10,7 +10,7 @@
 // one division by l finishes each row. The N x N matrix never leaves
 // registers.
 //
-// gfx950 mapping (per wave of 64 lanes, 32*QT query rows):
+// gfx950 mapping (per wave of 64 lanes, 32 query rows):
 //   * Scores are formed transposed, S^T = K Q^T, on the matrix cores: the
 //     accumulator layout then gives every lane one query column and 16 keys,
 //     so the row max and row sum are in-lane loops plus one exchange with the
@@ -19,15 +19,17 @@
 //     of O^T += V^T P^T; V^T comes from the row-major V tile in LDS through
 //     the transposing LDS read, with the contraction (key) order chosen to
 //     match the accumulator layout.
-//   * Q stays in registers for the whole kernel; K and V tiles are staged
-//     HBM -> registers -> LDS one block ahead (double-buffered LDS).
+//   * Q stays in registers for the whole kernel; K and V tiles go HBM -> LDS
+//     by DMA one block ahead (double-buffered LDS), and each product reads
+//     its LDS fragments one k-step ahead.
 //   * Base-2 exponentials with scale*log2(e) folded into one FMA; the
 //     denominator l is summed from the unrounded float32 probabilities.
 //   * Causal: key blocks past the diagonal are never visited; only blocks
 //     that cross the diagonal (or the ragged tail) are masked element-wise.
 //   * Grid order: heaviest causal query blocks first; all query blocks of a
-//     head go to the same XCD (workgroups are dealt round-robin to the 8
-//     XCDs) so that its K/V stream is shared through one L2.
+//     key/value head (of every query head that shares it) go to the same XCD
+//     (workgroups are dealt round-robin to the 8 XCDs) so that its K/V
+//     stream is shared through one L2.
 #include <type_traits>
 
 #include "fa_device.hpp"
