@@ -38,8 +38,7 @@
 
 namespace fa {
 
-// Maps the linear workgroup id to (bh, qb): heavy-first query blocks, and
-// when BH is a multiple of 8 every query block of head bh runs on XCD bh % 8.
+// Output stores of 4 consecutive elements in the output dtype.
 template <typename T> struct OutStore;
 template <> struct OutStore<bf16> {
   static __device__ __forceinline__ void store4(bf16* dst, float a, float b, float c, float d) {
