@@ -68,7 +68,7 @@ def _roofline(kernel, kind, flops, mean_ms):
             "algorithmic_flop_per_launch": flops, "mean_launch_ms": mean_ms}
 
 
-def cpu_baseline(w, rows_per_head=1536):
+def cpu_baseline(w, rows_per_head=4096):
     """The float64 oracle on host cores, on a bounded sample of the same workload.
 
     Sample: `rows_per_head` seeded query rows of every head, each against all
