@@ -66,3 +66,22 @@ def test_deterministic():
     b = gpu_backward(inp, True)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_bench_size_backward_two_heads():
+    """The timed workload itself (B=1 H=32 N=16384 d=128 causal, the launch
+    configuration bench.py measures): every element of dQ, dK, dV of two heads
+    against the oracle, and the gradient-sum invariants on all 32 heads."""
+    B, H, N, d, seed = 1, 32, 16384, 128, 3
+    heads = [(0, 0), (0, 21)]
+    print(f"case bench-size backward B={B} H={H} N={N} d={d} seed={seed} heads={heads}", flush=True)
+    inp = inputs.make_inputs(B, H, N, d, seed, "bf16", with_do=True)
+    dq, dk, dv = gpu_backward(inp, True)
+    ref = oracle_backward(inp, True, heads=heads)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        for b, h in heads:
+            mx, rms = assert_close(g[b, h], r[b, h], "bf16", f"{name}[{b},{h}]")
+            print(f"  {name}[{b},{h}]: max={mx:.3g} rms={rms:.3g}", flush=True)
+    do = inp["do"].double().numpy()
+    assert np.max(np.abs(dk.sum(axis=2))) <= 1e-1
+    assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 1e-1

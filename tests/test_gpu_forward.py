@@ -36,17 +36,20 @@ def test_workload_bf16_b4h16_n2048_d64(causal):
     _run_full(w["B"], w["H"], w["N"], w["d"], w["seed"], "bf16", causal)
 
 
-def test_workload_bf16_causal_n16384_d128_sampled():
-    """bf16, B=1 H=32 N=16384 d=128 causal: 512 seeded query rows per head vs the oracle over all keys."""
+@pytest.mark.parametrize("o_dtype", ["bf16", "f32"])
+def test_workload_bf16_causal_n16384_d128_sampled(o_dtype):
+    """bf16, B=1 H=32 N=16384 d=128 causal: 512 seeded query rows per head vs
+    the oracle over all keys, with the bf16 O of the headline forward and the
+    float32 O of the forward that feeds the backward (both timed by bench.py)."""
     w = inputs.WORKLOADS["fwd_bf16_causal_b1h32_n16384_d128"]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     inp = inputs.make_inputs(B, H, N, d, w["seed"], "bf16")
     rows = inputs.sample_rows(w["seed"], B, H, N, w["sample"])
-    print(f"case {w} sampled", flush=True)
-    o, lse = gpu_forward(inp, "bf16", True)
+    print(f"case {w} sampled o={o_dtype}", flush=True)
+    o, lse = gpu_forward(inp, "bf16", True, o_dtype)
     ro, rl = oracle_forward(inp, "bf16", True, rows=rows)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    mx, rms = assert_close(gather_rows(o, rows), ro, "bf16", "O", o_bf16=True)
+    mx, rms = assert_close(gather_rows(o, rows), ro, "bf16", "O", o_bf16=(o_dtype == "bf16"))
     le = assert_lse(gather_rows(lse, rows), rl, "lse")
     print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
 
