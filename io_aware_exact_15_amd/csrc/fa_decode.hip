@@ -293,13 +293,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
 }
 
 // One wave per output row (b, h, i): merges the ns partials of its tile
-// column. Lane p < ns holds partial p's m and l for the weights; for the
-// output every lane holds D / 64 consecutive dimensions.
+// column, 64 at a time: lane j holds partial j's m and weight, every lane
+// holds D / 64 consecutive dimensions of the output, and the partials'
+// accumulator loads are issued 8 at a time so that they overlap.
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParts parts, OutT* __restrict__ O,
                                                            float* __restrict__ LSE, int B, int H, int Hkv, int Nq,
                                                            int nqt, int ns) {
-  constexpr int E = D / 64;
+  constexpr int E = D / 64, U = 8;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= (long)B * H * Nq) return;
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParts parts, Ou
   const int G = H / Hkv, kvh = h / G, r = (h % G) * Nq + ti;
   const int qt = r / 32, col = r % 32;
   const size_t p0 = (((size_t)b * Hkv + kvh) * nqt + qt) * ns;
-  // Global max over the partials (64 at a time across the lanes).
+  // Global max over the partials.
   float M = kNegInf;
   for (int p = lane; p < ns; p += 64) M = fmaxf(M, parts.ml[(p0 + p) * 64 + col]);
 #pragma unroll
@@ -317,14 +318,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParts parts, Ou
   float L = 0.f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int p = 0; p < ns; ++p) {
-    const float mp = parts.ml[(p0 + p) * 64 + col];
-    const float w = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);  // no visible key in that split
-    L += w * parts.ml[(p0 + p) * 64 + 32 + col];
-    const float* a = parts.acc + ((p0 + p) * 32 + col) * D + E * lane;
+  for (int c0 = 0; c0 < ns; c0 += 64) {
+    // lane j: weight of partial c0 + j (0 past ns or with no visible key in that split)
+    const int pj = c0 + lane;
+    float w = 0.f;
+    if (pj < ns) {
+      const float mp = parts.ml[(p0 + pj) * 64 + col];
+      w = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+      L += w * parts.ml[(p0 + pj) * 64 + 32 + col];
+    }
+    const int nc = min(64, ns - c0);
+    for (int j0 = 0; j0 < nc; j0 += U) {
+      float a[U][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += w * a[e];
+      for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u, nc - 1);  // in range; duplicates get weight 0 below
+        const float* src = parts.acc + ((p0 + c0 + j) * 32 + col) * D + E * lane;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[u][e] = src[e];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = __shfl(w, j0 + u, 64);
+        const float wk = (j0 + u < nc) ? wu : 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += wk * a[u][e];
+      }
+    }
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
   const float inv = 1.f / L;
   OutT* dst = O + row * D + E * lane;
 #pragma unroll
