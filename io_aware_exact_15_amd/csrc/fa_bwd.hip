@@ -459,9 +459,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
   const int hi = lane >> 5, col = lane & 31;
   const size_t hoff = (size_t)bh * N * D;         // query head: Q, dO, dQ
   const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head: K, V
-  const int qw = qb * BR + 32 * wave;
-  const int q = qw + col;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int qw = qb * BR + 32 * wave_u;  // wave-uniform: the mask test below is a scalar branch
+  const int q = qw + col;
 
   const i32x4 kr = make_rsrc(ws.k + kvoff, (unsigned)N * ROWB);
   const i32x4 vr = make_rsrc(ws.v + kvoff, (unsigned)N * ROWB);
@@ -552,23 +552,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // P and dS^T -> fp16 B fragments. Only blocks that cross the diagonal or
+    // the ragged tail take the masked copy (need_mask is wave-uniform).
     f16x8 df[NKT][2];
+    auto ds_tiles = [&](auto masked_c) __attribute__((always_inline)) {
+      constexpr bool masked = decltype(masked_c)::value;
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      float dsv[16];
-      // key k0 + 32 kt + 8 (i/4) + 4 hi + i % 4 is kept iff its offset 8 (i/4) + i % 4 <= lim
-      const int lim = min(CAUSAL ? q : N - 1, N - 1) - (k0 + 32 * kt) - 4 * hi;
+      for (int kt = 0; kt < NKT; ++kt) {
+        float dsv[16];
+        // key k0 + 32 kt + 8 (i/4) + 4 hi + i % 4 is kept iff its offset 8 (i/4) + i % 4 <= lim
+        const int lim = min(CAUSAL ? q : N - 1, N - 1) - (k0 + 32 * kt) - 4 * hi;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(s[kt][i], cS, nl));
-        if (need_mask && 8 * (i / 4) + (i % 4) > lim) p = 0.f;
-        dsv[i] = p * ((SCALED ? dp[kt][i] * sPV : dp[kt][i]) - dq_d);
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(__builtin_fmaf(s[kt][i], cS, nl));
+          if (masked && 8 * (i / 4) + (i % 4) > lim) p = 0.f;
+          dsv[i] = p * ((SCALED ? dp[kt][i] * sPV : dp[kt][i]) - dq_d);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          df[kt][h2] = f16x8{(f16)dsv[8 * h2], (f16)dsv[8 * h2 + 1], (f16)dsv[8 * h2 + 2], (f16)dsv[8 * h2 + 3],
+                             (f16)dsv[8 * h2 + 4], (f16)dsv[8 * h2 + 5], (f16)dsv[8 * h2 + 6], (f16)dsv[8 * h2 + 7]};
       }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        df[kt][h2] = f16x8{(f16)dsv[8 * h2], (f16)dsv[8 * h2 + 1], (f16)dsv[8 * h2 + 2], (f16)dsv[8 * h2 + 3],
-                           (f16)dsv[8 * h2 + 4], (f16)dsv[8 * h2 + 5], (f16)dsv[8 * h2 + 6], (f16)dsv[8 * h2 + 7]};
-    }
+    };
+    if (need_mask) ds_tiles(std::true_type{});
+    else ds_tiles(std::false_type{});
     // dQ^T += K^T dS^T: K^T read transposed, key order of the accumulator
     // rows; 16-key steps outer with the next step's reads issued first.
     constexpr int NST = 2 * NKT;

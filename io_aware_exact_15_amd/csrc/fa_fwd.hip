@@ -100,12 +100,12 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   const int hi = lane >> 5, col = lane & 31;
   const size_t hoff = (size_t)bh * N * D;         // query head
   const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head
-  const int qw = qb * BR + 32 * wave;  // first query row of this wave
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int qw = qb * BR + 32 * wave_u;  // first query row of this wave (wave-uniform: scalar branches below)
   const int q = qw + col;
 
   const i32x4 kr = make_rsrc(K + kvoff, (unsigned)N * ROWB);
   const i32x4 vr = make_rsrc(V + kvoff, (unsigned)N * ROWB);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // Load addressing: instruction n of this wave fills tile chunks
   // 64 (NI wave + n) + lane, i.e. row p / CPR, physical chunk p % CPR, which

@@ -74,9 +74,9 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   const int hi = lane >> 5, col = lane & 31;
   const size_t hoff = (size_t)bh * N * D;         // query head
   const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head
-  const int qw = qb * BR + 32 * wave;
-  const int q = qw + col;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int qw = qb * BR + 32 * wave_u;  // wave-uniform: scalar branches below
+  const int q = qw + col;
   const float s_v = descale[2];
   const float c = scale * descale[0] * descale[1] * kLog2e;
 
