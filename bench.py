@@ -101,17 +101,20 @@ PEAK_F32_MFMA_TFLOPS = 157.3
 
 
 def _median_ms(torch, fn, iters, warmup):
+    """Median and min of the per-call GPU time: the calls are enqueued back to
+    back (as in the headline loop), each between its own pair of events, and
+    the host synchronises once at the end, so host launch latency does not
+    land inside the timed intervals."""
     for _ in range(warmup):
         fn()
-    ts = []
-    for _ in range(iters):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for e0, e1 in evs:
         e0.record()
         fn()
         e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    ts.sort()
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     return ts[len(ts) // 2], ts[0]
 
 
