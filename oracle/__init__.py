@@ -11,6 +11,8 @@ from .attention import (  # noqa: F401
     forward,
     forward_quantized,
     backward,
+    backward_rows,
+    backward_causal_tail,
     forward_gqa,
     backward_gqa,
     forward_decode,

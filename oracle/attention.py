@@ -54,6 +54,7 @@ import numpy as np
 
 __all__ = [
     "scores", "probabilities", "forward", "forward_quantized", "backward",
+    "backward_rows", "backward_causal_tail",
     "forward_gqa", "backward_gqa", "forward_decode", "backward_quantized",
     "online_softmax_chunked", "brute_force_forward", "brute_force_backward",
     "decode_e4m3fn", "decode_e5m2",
@@ -214,6 +215,59 @@ def backward(q, k, v, do, scale, causal, heads=None):
         dq[b, h] = c * (ds @ k[b, h])
         dk[b, h] = c * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def backward_rows(q, k, v, do, scale, causal, rows):
+    """dQ at the listed query rows only, for sequences too long for `backward`.
+
+    Everything the chain rule needs for dQ_i lives in row i: its softmax row
+    P_i (all keys, masked by the row's own position), dP_i = dO_i V^T,
+    D_i = sum_j P_ij dP_ij, dS_i = P_i * (dP_i - D_i), and dQ_i = c dS_i K --
+    the formulas of `backward` restricted to those rows.
+    rows: int array [B, H, R] of query positions. Returns float64 [B, H, R, d].
+    """
+    c = float(np.float32(scale))
+    rows = np.asarray(rows)
+    B, H = rows.shape[:2]
+    out = np.empty((B, H, rows.shape[-1], q.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            idx = rows[b, h]
+            kh = _f64(k[b, h])
+            p_rows, _, _ = _softmax_rows(scores(_f64(q[b, h][idx]), kh, scale, causal, idx))
+            dp_rows = _f64(do[b, h][idx]) @ _f64(v[b, h]).T
+            d_rows = np.sum(p_rows * dp_rows, axis=1, keepdims=True)
+            ds_rows = p_rows * (dp_rows - d_rows)
+            out[b, h] = c * (ds_rows @ kh)
+    return out
+
+
+def backward_causal_tail(q, k, v, do, scale, ntail):
+    """dK and dV of the last `ntail` keys under the causal mask.
+
+    With the mask, key j receives gradient only from query rows i >= j, so
+    the last T keys are reached by the last T rows alone. Those rows' full
+    softmax rows (every key they see) give P, dP, D and dS exactly as in
+    `backward`; dK and dV of the tail keys are then the tail columns of
+    c dS^T Q and P^T dO over those rows.
+    Returns (dK, dV) float64 [B, H, T, d] for keys N - T .. N - 1.
+    """
+    c = float(np.float32(scale))
+    B, H, N, _ = q.shape
+    t0 = N - ntail
+    idx = np.arange(t0, N)
+    dk = np.empty((B, H, ntail, k.shape[-1]))
+    dv = np.empty((B, H, ntail, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            qt, dot = _f64(q[b, h][t0:]), _f64(do[b, h][t0:])
+            p_t, _, _ = _softmax_rows(scores(qt, _f64(k[b, h]), scale, True, idx))
+            dp_t = dot @ _f64(v[b, h]).T
+            d_t = np.sum(p_t * dp_t, axis=1, keepdims=True)
+            ds_t = p_t * (dp_t - d_t)
+            dk[b, h] = c * (ds_t[:, t0:].T @ qt)
+            dv[b, h] = p_t[:, t0:].T @ dot
+    return dk, dv
 
 
 def _group(q, k):

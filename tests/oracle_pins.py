@@ -444,6 +444,42 @@ def pin_quantized_backward(o):
     assert o.decode_e5m2(np.uint8(0x3F)) == 1.75
 
 
+def _torch_grads(q, k, v, do, c, causal):
+    """torch's float64 CPU attention and autograd: (dQ, dK, dV) as numpy."""
+    import torch
+    import torch.nn.functional as F
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=c).backward(torch.tensor(do))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_backward_rows_torch(o):
+    """X8: dQ at chosen rows equals those rows of torch's autograd dQ (rows
+    out of order and with gaps, so a mask built from 0..R-1 would fail)."""
+    B, H, N, d, seed = 1, 2, 37, 16, 40
+    q, k, v, do = _qkv(seed, B, H, N, d)
+    c = float(np.float32(1.0 / math.sqrt(d)))
+    rows = np.array([[[36, 0, 17, 5, 30]], [[1, 2, 35, 20, 9]]]).reshape(B, H, 5)
+    for causal in (False, True):
+        ref = _torch_grads(q, k, v, do, c, causal)[0]
+        got = o.backward_rows(q, k, v, do, c, causal, rows)
+        for h in range(H):
+            assert np.max(np.abs(got[0, h] - ref[0, h][rows[0, h]])) <= 1e-10, (causal, h)
+
+
+def pin_causal_tail_torch(o):
+    """X9: dK, dV of the last T keys under the causal mask equal the last T
+    rows of torch's autograd dK, dV (T = 1, a few, and all keys)."""
+    B, H, N, d, seed = 2, 1, 29, 8, 41
+    q, k, v, do = _qkv(seed, B, H, N, d)
+    c = float(np.float32(1.0 / math.sqrt(d)))
+    _, rk, rv = _torch_grads(q, k, v, do, c, True)
+    for t in (1, 6, N):
+        dk, dv = o.backward_causal_tail(q, k, v, do, c, t)
+        assert np.max(np.abs(dk - rk[:, :, N - t:])) <= 1e-10, t
+        assert np.max(np.abs(dv - rv[:, :, N - t:])) <= 1e-10, t
+
+
 ALL_PINS = [
     pin_hand_example, pin_rows_sum_to_one, pin_chunked_equals_full, pin_constant_column,
     pin_uniform_scores, pin_brute_force, pin_torch_sdpa, pin_finite_differences,
@@ -451,4 +487,5 @@ ALL_PINS = [
     pin_masked_chunk, pin_sampled_rows, pin_e4m3_decode, pin_quantized_forward,
     pin_gqa_torch, pin_gqa_brute_force, pin_gqa_finite_differences, pin_decode_torch,
     pin_decode_is_tail_of_full, pin_e5m2_decode, pin_quantized_forward_e5m2, pin_quantized_backward,
+    pin_backward_rows_torch, pin_causal_tail_torch,
 ]

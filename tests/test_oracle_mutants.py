@@ -45,6 +45,11 @@ MUTANTS = {
                             "return forward(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1)), scale, causal, rows)"),
     "gqa_dk_first_head_only": ("dke.reshape(B, Hkv, G, N, d).sum(axis=2)", "dke.reshape(B, Hkv, G, N, d)[:, :, 0]"),
     "decode_top_left_mask": ("pos = np.arange(Nk - Nq, Nk)", "pos = np.arange(Nq)"),
+    "rows_missing_D_term": ("ds_rows = p_rows * (dp_rows - d_rows)", "ds_rows = p_rows * dp_rows"),
+    "rows_mask_by_rank": ("scores(_f64(q[b, h][idx]), kh, scale, causal, idx)",
+                          "scores(_f64(q[b, h][idx]), kh, scale, causal)"),
+    "tail_dv_uses_ds": ("dv[b, h] = p_t[:, t0:].T @ dot", "dv[b, h] = ds_t[:, t0:].T @ dot"),
+    "tail_mask_from_zero": ("scores(qt, _f64(k[b, h]), scale, True, idx)", "scores(qt, _f64(k[b, h]), scale, True)"),
     "decode_head_map_modulo": ("scores(q[b, h], k[b, h // G], scale, causal, pos)",
                                "scores(q[b, h], k[b, h % k.shape[1]], scale, causal, pos)"),
 }
