@@ -35,6 +35,13 @@
 // magnitude lies in fp16's normal range (2^-14 .. 65504; smaller values keep
 // fp16's subnormal precision, 2^-24), and P and dS, which must be rounded
 // for the products, keep 3 more significant bits than bf16 would give them.
+// P enters dV = P^T dO multiplied by 2^15 (kPScale; P <= 1, so at most
+// 32768): over long rows attention spreads thin (P ~ 1/N), and unscaled
+// probabilities below 2^-14 would fall into fp16's subnormal range and lose
+// relative precision. The factor rides in the exponent (the workspace holds
+// NL = 15 - lse log2 e) and leaves dV with one multiply by 2^-15 at the end;
+// D is stored times 2^-15 so that dS = 2^15 P (2^-15 dP - 2^-15 D) keeps its
+// true scale at the same instruction count.
 // Accumulation is float32 throughout.
 //
 // LDS tiles use the forward pass's XOR swizzle (16-byte chunk c of row r at
@@ -74,9 +81,12 @@ __device__ __forceinline__ int swz_b(int r) {
 // Same XCD-aware, heavy-first order as the forward pass; first_is_heavy
 // selects whether block index 0 (dK/dV, causal) or nb-1 (dQ) is heaviest.
 // Workspace layout (all offsets 256-byte aligned): D [q_rows] f32,
-// NL = -lse*log2(e) [q_rows] f32, Q [q_rows, d] fp16, K and V [kv_rows, d]
+// NL = kPScale - lse*log2(e) [q_rows] f32 (D is stored times 2^-kPScale),
+// Q [q_rows, d] fp16, K and V [kv_rows, d]
 // fp16, dO [q_rows, d] fp16, and when q_rows > kv_rows (grouped heads)
 // per-query-head dK and dV [q_rows, d] f32. q_rows = B*H*N, kv_rows = B*Hkv*N.
+constexpr float kPScale = 15.f;            // P is scaled by 2^kPScale for the dV product
+constexpr float kPScaleInv = 1.f / 32768.f;  // 2^-kPScale
 struct BwdWs {
   float* Dv;
   float* NL;
@@ -184,8 +194,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
 #pragma unroll
   for (int s = L / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (row < rows && part == 0) {
-    ws.Dv[row] = FDO == 0 ? acc : acc * desc[3];
-    ws.NL[row] = -LSE[row] * kLog2e;
+    ws.Dv[row] = (FDO == 0 ? acc : acc * desc[3]) * kPScaleInv;
+    ws.NL[row] = kPScale - LSE[row] * kLog2e;
   }
 }
 
@@ -219,12 +229,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
   __shared__ __attribute__((aligned(1024))) char lds_v[VTB];
   __shared__ __attribute__((aligned(1024))) char lds[NST][STB];
 
-  float cS = c, sPV = 1.f, fK = scale, fV = 1.f;
+  // p below is 2^15 P; sPV carries the matching 2^-15 (and the FP8 scales), fV undoes it on dV.
+  float cS = c, sPV = kPScaleInv, fK = scale, fV = kPScaleInv;
   if (SCALED) {
     cS = c * desc[0] * desc[1];
-    sPV = desc[3] * desc[2];
+    sPV = desc[3] * desc[2] * kPScaleInv;
     fK = scale * desc[0];
-    fV = desc[3];
+    fV = desc[3] * kPScaleInv;
   }
   int bh, kb;
   map_head_block(blockIdx.x, BH, G, nkb, CAUSAL, bh, kb);
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdWs ws, float* __res
         float p = fast_exp2(__builtin_fmaf(s[4 * g + r], cS, l4[r]));
         if (masked && key > q0 + 8 * g + 4 * hi + r) p = 0.f;
         pv[4 * g + r] = p;
-        dsv[4 * g + r] = p * ((SCALED ? dp[4 * g + r] * sPV : dp[4 * g + r]) - d4[r]);
+        dsv[4 * g + r] = p * __builtin_fmaf(dp[4 * g + r], sPV, -d4[r]);  // P (dP - D)
       }
     }
     f16x8 pf[2], df[2];
@@ -509,8 +520,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdWs ws, float* __restr
       of[ks] = q < N ? b : f16x8{};
     }
   }
-  const float nl = q < N ? ws.NL[(size_t)bh * N + q] : 0.f;
-  const float dq_d = q < N ? ws.Dv[(size_t)bh * N + q] : 0.f;
+  // The workspace's 2^15 on P and 2^-15 on D are for the dK/dV kernel; here P is unscaled.
+  const float nl = q < N ? ws.NL[(size_t)bh * N + q] - kPScale : 0.f;
+  const float dq_d = q < N ? ws.Dv[(size_t)bh * N + q] * 32768.f : 0.f;
   f32x16 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
