@@ -111,7 +111,7 @@ def fa_forward(q, k, v, o, lse, scale, causal, stream=None):
 
 
 def fa_forward_typed(in_dtype, o_dtype, q, k, v, descale, o, lse, scale, causal, stream=None):
-    """Forward with in_dtype in {FA_F32, FA_BF16, FA_FP8_E4M3}; descale: device float32[3] or None."""
+    """Forward with in_dtype in {FA_F32, FA_BF16, FA_FP8_E4M3, FA_FP8_E5M2}; descale: device float32[3] or None."""
     B, H, N, d = _dims(q)
     _check(lib().fa_forward_typed(int(in_dtype), int(o_dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(descale),
                                   _ptr(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),

@@ -118,3 +118,34 @@ def test_deterministic():
     o1, l1 = gpu_forward(inp, "bf16", True)
     o2, l2 = gpu_forward(inp, "bf16", True)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("side_stream", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+def test_plain_entry_point(causal, side_stream):
+    """fa_forward itself (bf16 in and out, the plain signature), on the
+    current stream or on a caller-made stream: the same bits as
+    fa_forward_typed(BF16, BF16) and the oracle's values."""
+    from io_aware_exact_15_amd import binding as fa
+    B, H, N, d = 2, 4, 777, 128
+    print(f"case fa_forward B={B} H={H} N={N} d={d} causal={causal} side_stream={side_stream}", flush=True)
+    inp = inputs.make_inputs(B, H, N, d, 14, "bf16")
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in "qkv")
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+    if side_stream:
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        fa.fa_forward(q, k, v, o, lse, 1.0 / math.sqrt(d), causal, stream=st)
+        st.synchronize()
+    else:
+        fa.fa_forward(q, k, v, o, lse, 1.0 / math.sqrt(d), causal)
+        torch.cuda.synchronize()
+    got_o, got_l = o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+    typed_o, typed_l = gpu_forward(inp, "bf16", causal)
+    assert np.array_equal(got_o, typed_o) and np.array_equal(got_l, typed_l)
+    ro, rl = oracle_forward(inp, "bf16", causal)
+    mx, rms = assert_close(got_o, ro, "bf16", "O", o_bf16=True)
+    le = assert_lse(got_l, rl, "lse")
+    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
