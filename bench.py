@@ -96,6 +96,68 @@ def cpu_baseline(w, rows_per_head=4096):
     }
 
 
+def cpu_baseline_sample(kind, w, inp, causal, target_flop=5e10):
+    """The float64 oracle timed on a bounded sample of one workload, for the
+    per-workload lines of --configs (a few seconds each).
+
+    kind: "fwd" (seeded query rows of every head against all their keys),
+    "bwd" (the full backward of the first head group), or "decode" (the whole
+    decode step). Value: the algorithmic FLOP of what was computed per second
+    of oracle wall time.
+    """
+    import numpy as np
+
+    import oracle
+    from io_aware_exact_15_amd import inputs
+
+    B, H, d = w["B"], w["H"], w["d"]
+    Hkv = w.get("Hkv", H)
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(d)
+    dtype = w["dtype"]
+    arr = {n: inputs.to_numpy(inp[n]) for n in ("q", "k", "v", "do") if n in inp}
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    if kind == "decode":
+        Nq, Nk = w["Nq"], w["Nk"]
+        oracle.forward_decode(arr["q"], arr["k"], arr["v"], scale, causal)
+        pos = np.arange(Nk - Nq, Nk)
+        keys = np.minimum(pos + 1, Nk) if causal else np.full(Nq, Nk)
+        flop = 4.0 * d * B * H * float(np.sum(keys))
+        sample = f"the whole decode step ({B * H * Nq} rows against {Nk} keys)"
+    elif kind == "fwd":
+        N = w["N"]
+        per_row = 4.0 * d * N * B * H
+        R = int(min(N, max(1, target_flop // per_row)))
+        rows = inputs.sample_rows(w["seed"], B, H, N, R)
+        if dtype == "fp8":
+            oracle.forward_quantized(arr["q"], arr["k"], arr["v"], inp["sq"], inp["sk"], inp["sv"], scale, causal, rows)
+        elif G > 1:
+            oracle.forward_gqa(arr["q"], arr["k"], arr["v"], scale, causal, rows)
+        else:
+            oracle.forward(arr["q"], arr["k"], arr["v"], scale, causal, rows)
+        flop = float(np.sum(4.0 * d * (rows + 1))) if causal else 4.0 * d * N * rows.size
+        sample = f"{R} seeded query rows per head x {B * H} heads against all their keys"
+    else:  # bwd: the first head group (G query heads and their key/value head) of batch 0
+        N = w["N"]
+        sl = lambda x, h: x[:1, :h]  # noqa: E731
+        if dtype == "fp8bwd":
+            oracle.backward_quantized(sl(arr["q"], 1), sl(arr["k"], 1), sl(arr["v"], 1), sl(arr["do"], 1),
+                                      inp["sq"], inp["sk"], inp["sv"], inp["sdo"], scale, causal)
+            heads = 1
+        elif G > 1:
+            oracle.backward_gqa(sl(arr["q"], G), sl(arr["k"], 1), sl(arr["v"], 1), sl(arr["do"], G), scale, causal)
+            heads = G
+        else:
+            oracle.backward(sl(arr["q"], 1), sl(arr["k"], 1), sl(arr["v"], 1), sl(arr["do"], 1), scale, causal)
+            heads = 1
+        flop = _flops(1, heads, N, d, causal, "bwd")
+        sample = f"full backward of {heads} head(s)"
+    dt = time.perf_counter() - t0
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample}, float64 numpy ({dt:.2f} s wall)"}
+
+
 PEAK_FP8_TFLOPS = 5033.2
 PEAK_F32_MFMA_TFLOPS = 157.3
 
@@ -118,7 +180,7 @@ def _median_ms(torch, fn, iters, warmup):
     return ts[len(ts) // 2], ts[0]
 
 
-def run_configs(iters=20, warmup=3):
+def run_configs(iters=20, warmup=3, with_cpu=True):
     """Times every workload of the path (one JSON line per workload and pass)."""
     import torch
 
@@ -147,9 +209,12 @@ def run_configs(iters=20, warmup=3):
             fwd = lambda: fa.fa_forward_gqa(in_t, o_t, q, k, v, desc, o, lse, scale, causal)
             med, mn = _median_ms(torch, fwd, iters, warmup)
             f = _flops(B, H, N, d, causal, "fwd")
-            print(json.dumps({"workload": name, "pass": "fwd", "causal": causal, "dtype": w["dtype"],
-                              "ms_median": med, "ms_min": mn, "tflops": f / (med * 1e-3) / 1e12,
-                              "frac_of_peak": f / (med * 1e-3) / 1e12 / peak, "peak_tflops": peak}), flush=True)
+            line = {"workload": name, "pass": "fwd", "causal": causal, "dtype": w["dtype"],
+                    "ms_median": med, "ms_min": mn, "tflops": f / (med * 1e-3) / 1e12,
+                    "frac_of_peak": f / (med * 1e-3) / 1e12 / peak, "peak_tflops": peak}
+            if with_cpu:
+                line["cpu_baseline"] = cpu_baseline_sample("fwd", w, inp, causal)
+            print(json.dumps(line), flush=True)
             if w["backward"]:
                 do = inp["do"].to(dev)
                 dq = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
@@ -159,17 +224,19 @@ def run_configs(iters=20, warmup=3):
                 bwd = lambda: fa.fa_backward_gqa(q, k, v, o, fa.FA_F32, do, lse, dq, dk, dv, ws, scale, causal)
                 bmed, bmn = _median_ms(torch, bwd, iters, warmup)
                 bf = _flops(B, H, N, d, causal, "bwd")
-                print(json.dumps({"workload": name, "pass": "bwd", "causal": causal, "dtype": w["dtype"],
-                                  "ms_median": bmed, "ms_min": bmn, "tflops": bf / (bmed * 1e-3) / 1e12,
-                                  "frac_of_peak": bf / (bmed * 1e-3) / 1e12 / peak, "peak_tflops": peak}),
-                      flush=True)
+                line = {"workload": name, "pass": "bwd", "causal": causal, "dtype": w["dtype"],
+                        "ms_median": bmed, "ms_min": bmn, "tflops": bf / (bmed * 1e-3) / 1e12,
+                        "frac_of_peak": bf / (bmed * 1e-3) / 1e12 / peak, "peak_tflops": peak}
+                if with_cpu:
+                    line["cpu_baseline"] = cpu_baseline_sample("bwd", w, inp, causal)
+                print(json.dumps(line), flush=True)
                 print(json.dumps({"workload": name, "pass": "fwd+bwd", "causal": causal, "dtype": w["dtype"],
                                   "ms_median": med + bmed,
                                   "tflops": (f + bf) / ((med + bmed) * 1e-3) / 1e12,
                                   "frac_of_peak": (f + bf) / ((med + bmed) * 1e-3) / 1e12 / peak}), flush=True)
 
 
-def run_fp8_bwd_configs(iters=20, warmup=3):
+def run_fp8_bwd_configs(iters=20, warmup=3, with_cpu=True):
     """Times the FP8 backward workloads (E4M3 Q, K, V; E5M2 dO). The forward
     that feeds them runs in float32 on the dequantised values (untimed)."""
     import numpy as np
@@ -197,13 +264,16 @@ def run_fp8_bwd_configs(iters=20, warmup=3):
                                               codes["do"], desc, o, fa.FA_F32, lse, dq, dk, dv, ws, scale, causal)
             med, mn = _median_ms(torch, fn, iters, warmup)
             bf = _flops(B, H, N, d, causal, "bwd")
-            print(json.dumps({"workload": name, "pass": "bwd", "causal": causal, "dtype": "fp8 e4m3 / e5m2 dO",
-                              "ms_median": med, "ms_min": mn, "tflops": bf / (med * 1e-3) / 1e12,
-                              "frac_of_peak": bf / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                              "peak_tflops": PEAK_BF16_TFLOPS, "note": "fp16 matrix-core operands"}), flush=True)
+            line = {"workload": name, "pass": "bwd", "causal": causal, "dtype": "fp8 e4m3 / e5m2 dO",
+                    "ms_median": med, "ms_min": mn, "tflops": bf / (med * 1e-3) / 1e12,
+                    "frac_of_peak": bf / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                    "peak_tflops": PEAK_BF16_TFLOPS, "note": "fp16 matrix-core operands"}
+            if with_cpu:
+                line["cpu_baseline"] = cpu_baseline_sample("bwd", w, inp, causal)
+            print(json.dumps(line), flush=True)
 
 
-def run_decode_configs(iters=20, warmup=3):
+def run_decode_configs(iters=20, warmup=3, with_cpu=True):
     """Times the decode workloads (HBM-bound: reported as GB/s of the
     algorithmic bytes, the K/V cache read once plus Q, O and lse)."""
     import torch
@@ -223,9 +293,12 @@ def run_decode_configs(iters=20, warmup=3):
         med, mn = _median_ms(torch, fn, iters, warmup)
         nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
         gbs = nbytes / (med * 1e-3) / 1e9
-        print(json.dumps({"workload": name, "pass": "decode", "causal": w["causal"], "dtype": "bf16",
-                          "ms_median": med, "ms_min": mn, "algorithmic_bytes": nbytes, "GB_per_s": gbs,
-                          "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}), flush=True)
+        line = {"workload": name, "pass": "decode", "causal": w["causal"], "dtype": "bf16",
+                "ms_median": med, "ms_min": mn, "algorithmic_bytes": nbytes, "GB_per_s": gbs,
+                "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+        if with_cpu:
+            line["cpu_baseline"] = cpu_baseline_sample("decode", w, inp, w["causal"])
+        print(json.dumps(line), flush=True)
 
 
 def main():
@@ -246,9 +319,9 @@ def main():
         sys.exit(2)
 
     if args.configs:
-        run_configs()
-        run_fp8_bwd_configs()
-        run_decode_configs()
+        run_configs(with_cpu=not args.no_cpu)
+        run_fp8_bwd_configs(with_cpu=not args.no_cpu)
+        run_decode_configs(with_cpu=not args.no_cpu)
         return
 
     import torch
