@@ -111,8 +111,11 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
  * The probabilities are recomputed block by block from Q, K and lse; no
  * N x N buffer exists at any time. The matrix-core operands are fp16: bf16
  * inputs are converted exactly while |x| lies in [2^-14, 65504]; smaller
- * magnitudes keep fp16's subnormal resolution (2^-24) and larger ones are
- * outside the supported range.
+ * magnitudes keep fp16's subnormal resolution (2^-24). Larger magnitudes in
+ * q, k, v or dO are outside the supported range: they overflow to infinity in
+ * the fp16 copies, and the gradients come out non-finite rather than silently
+ * wrong. The softmax probabilities enter the dV product scaled by 2^15, so
+ * they stay in fp16's normal range for any sequence length.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                 const void* dO, const float* lse, float* dq, float* dk, float* dv,
