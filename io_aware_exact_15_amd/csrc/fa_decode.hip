@@ -61,8 +61,10 @@ static inline void decode_split_shape(int B, int H, int Hkv, int Nq, int Nk, int
   const long tiles = (long)B * Hkv * nqt;
   const int nblk = (Nk + kDecBC - 1) / kDecBC;
   // About two workgroups per CU (one fits at a time: 128 KB of LDS), each
-  // streaming a long run of blocks.
+  // streaming a long run of blocks: at least 16 (2048 keys), so that a
+  // workgroup's ring prologue and merge epilogue stay a small part of it.
   long want = (512 + tiles - 1) / tiles;
+  if (want > nblk / 16) want = nblk / 16;
   if (want < 1) want = 1;
   if (want > nblk) want = nblk;
   sb = (nblk + (int)want - 1) / (int)want;  // blocks per split

@@ -48,9 +48,11 @@ def test_workload(name):
 EDGE = [
     (1, 1, 1, 1, 1, 64), (1, 4, 1, 1, 100, 128), (2, 8, 2, 3, 129, 64), (1, 32, 8, 1, 1000, 128),
     (1, 8, 8, 7, 257, 128), (1, 16, 2, 5, 300, 64), (2, 4, 4, 16, 16, 128), (1, 8, 1, 4, 5000, 128),
-    # one 32-row tile and long caches: 157 and 71 splits, so the merge walks its
-    # partials in chunks of 64 with a ragged last chunk
+    # one 32-row tile, medium caches: a handful of splits of 18 blocks each
     (1, 4, 1, 1, 20000, 128), (1, 2, 1, 2, 9000, 64),
+    # one 32-row tile and long caches: 92 and 65 splits, so the merge walks its
+    # partials in chunks of 64 with a ragged last chunk (of 28 and of 1)
+    (1, 4, 1, 1, 200003, 128), (1, 2, 1, 2, 140000, 64),
 ]
 
 
