@@ -54,9 +54,12 @@ template <> struct OutStore<float> {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 operands. 8 waves x 32 query rows (BR = 256) per workgroup, blocks of
-// BC keys (128 for the workloads here). Two waves share each SIMD, so one wave's softmax overlaps the
-// other's matrix-core work.
+// bf16 operands. NW waves x 32 query rows (BR = 32 NW) per workgroup, blocks
+// of BC keys. d = 128: 8 waves, 128-key blocks, one workgroup per CU (two
+// waves per SIMD, which is what the registers allow), so one wave's softmax
+// overlaps the other's matrix-core work. d = 64 halves the matrix work per
+// block but not the softmax, and needs fewer registers: 4 waves, 64-key
+// blocks and four workgroups per CU, four waves per SIMD.
 //
 // K/V tiles go HBM -> LDS with buffer loads that write LDS directly (no
 // staging registers; rows past N come back as zeros) into a 2-stage ring.
@@ -80,11 +83,11 @@ __device__ __forceinline__ int swz(int r) {
   return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);        // 8 chunks per row
 }
 
-template <int D, int BC, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
+template <int D, int BC, int NW, int LB, bool CAUSAL, typename OutT>
+__global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int BH, int G, int N, int nqb, float c) {
-  constexpr int NW = 8, BR = 32 * NW;
+  constexpr int BR = 32 * NW;
   constexpr int NKT = BC / 32;  // 32-key tiles per block
   constexpr int ROWB = 2 * D;          // bytes per tile row
   constexpr int TILEB = BC * ROWB;     // bytes per K (or V) tile
@@ -403,8 +406,9 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
 template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                               int G, int N, float c, hipStream_t st) {
-  const int nqb = (N + 255) / 256;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, 128, CAUSAL, OutT>), dim3(BH * nqb), dim3(512), 0, st, (const bf16*)q,
+  constexpr int NW = D == 64 ? 4 : 8, BC = D == 64 ? 64 : 128, LB = D == 64 ? 4 : 1;
+  const int nqb = (N + 32 * NW - 1) / (32 * NW);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, LB, CAUSAL, OutT>), dim3(BH * nqb), dim3(64 * NW), 0, st, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, G, N, nqb, c);
   return hipGetLastError();
 }
