@@ -68,14 +68,27 @@ template <> struct OutStore<float> {
 // rows at one column) and the transposing reads of V (ds_read_b64_tr_b16, 4
 // rows x 64 bytes) hit distinct LDS banks.
 //
-// Lazy rescaling: the running max m that the exponentials subtract is only
-// moved when a block's max exceeds it by more than kTau (log2 units). Until
-// then p = exp2(s*c - m) may reach 2^kTau, which bf16 and the float32
-// accumulators hold without loss, and since l and the accumulator share the
-// same m the final O = acc / l is unchanged. For typical data the max is
-// settled by the first block, and the per-block rescale of the 64 accumulator
-// registers disappears.
+// Lazy rescaling: the running max m that the exponentials subtract only
+// guards them against overflow and underflow. l and the accumulator share it,
+// so the final O = acc / l and lse do not depend on its value, and p =
+// exp2(s*c - m) may exceed 1 (bf16 and the float32 accumulators hold such p
+// without loss). Two forms:
+//   * d = 128: m moves only when a block's max exceeds it by more than kTau
+//     (log2 units). For typical data the max is settled by the first block,
+//     and the per-block rescale of the 64 accumulator registers disappears.
+//   * d = 64 (where the softmax weighs twice as much against the matrix work):
+//     the block max is formed only on key block 0, which every row sees, so
+//     every row's max gives p = 1 there and l >= 1 from then on (later
+//     probabilities that underflow are negligible against it). On later
+//     blocks p is taken with the m already held, and the lane's sum of its p
+//     (which bounds each of them, all being non-negative) is checked against
+//     kSumMax; a block that exceeds it (or overflows) is formed again with the
+//     max path. This saves the row max of every later block; at d = 128 the
+//     check, a branch on all of the block's exponentials, keeps the P.V
+//     products from starting under the last exponentials and costs more than
+//     it saves.
 constexpr float kTau = 8.f;
+constexpr float kSumMax = 256.f;
 
 template <int D>
 __device__ __forceinline__ int swz(int r) {
@@ -177,72 +190,159 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   const int nkb = CAUSAL ? min(nkb_all, q_last / BC + 1) : nkb_all;
 
   const char* const lb = &lds[0][0];
-  auto compute = [&](int kb, auto stage) {
+  // SUMCHECK selects the second form of the lazy rescale above. FIRST: key
+  // block 0, which every row of the wave sees (at least key 0).
+  constexpr bool SUMCHECK = D == 64;
+  enum { kNoMax, kExactMax };
+  auto compute = [&](int kb, auto stage, auto first) {
     constexpr int S = decltype(stage)::value;
+    constexpr bool FIRST = decltype(first)::value;
     const int k0 = kb * BC;
-    if (CAUSAL && k0 > qw + 31) return;  // every key of the block is after every query of the wave
-    f32x16 s[NKT];
+    if (CAUSAL && !FIRST && k0 > qw + 31) return;  // every key of the block is after every query of the wave
+    auto scores = [&](f32x16 (&s)[NKT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
-    // k-step outer: the NKT products of one step are independent, and the
-    // fragment reads of the next step are issued before them (the fences
-    // keep the scheduler from sinking the reads next to their use).
-    bf16x8 a[2][NKT];
+      for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
+      // k-step outer: the NKT products of one step are independent, and the
+      // fragment reads of the next step are issued before them (the fences
+      // keep the scheduler from sinking the reads next to their use).
+      bf16x8 a[2][NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) a[0][kt] = *(const bf16x8*)(lb + koff[S][0] + kt * 32 * ROWB);
+      for (int kt = 0; kt < NKT; ++kt) a[0][kt] = *(const bf16x8*)(lb + koff[S][0] + kt * 32 * ROWB);
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) {
-      if (kk + 1 < NKS) {
+      for (int kk = 0; kk < NKS; ++kk) {
+        if (kk + 1 < NKS) {
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+            a[(kk + 1) & 1][kt] = *(const bf16x8*)(lb + koff[S][kk + 1] + kt * 32 * ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma_bf16(a[kk & 1][kt], qf[kk], s[kt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
+        // key index of register i of tile kt: k0 + 32 kt + 8 (i / 4) + 4 hi + i % 4
+        const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 4 * hi;  // keep iff offset <= lim
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
-          a[(kk + 1) & 1][kt] = *(const bf16x8*)(lb + koff[S][kk + 1] + kt * 32 * ROWB);
-      }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma_bf16(a[kk & 1][kt], qf[kk], s[kt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
-      // key index of register i of tile kt: k0 + 32 kt + 8 (i / 4) + 4 hi + i % 4
-      const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 4 * hi;  // keep iff offset <= lim
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + (i % 4) > lim) s[kt][i] = kNegInf;
+      }
+    };
+    float rs0, rs1;
+    bf16x8 pf[NKT][2];
+    auto probs = [&](f32x16 (&s)[NKT], auto mode) __attribute__((always_inline)) {
+      constexpr int MODE = decltype(mode)::value;
+      if constexpr (MODE != kNoMax) {
+        float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < NKT; kt += 2)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            mx0 = fmaxf(fmaxf(mx0, s[kt][i]), s[kt][i + 1]);
+            mx1 = fmaxf(fmaxf(mx1, s[kt + 1][i]), s[kt + 1][i + 1]);
+          }
+        const float mx = pair_max(fmaxf(mx0, mx1)) * c;
+        const bool upd = mx > m;
+        if (__builtin_amdgcn_ballot_w64(upd)) {  // wave-uniform, rare after the first block
+          const float alpha = upd ? fast_exp2(m - mx) : 1.f;  // 0 while m is still -inf (l, acc are 0)
+          if (upd) m = mx;
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        }
+      }
+      const float nm = (m == kNegInf) ? 0.f : -m;
+      rs0 = 0.f;
+      rs1 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kt + 8 * (i / 4) + (i % 4) > lim) s[kt][i] = kNegInf;
-    }
-    float mx0 = kNegInf, mx1 = kNegInf;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float p[8];
 #pragma unroll
-    for (int kt = 0; kt < NKT; kt += 2)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        mx0 = fmaxf(fmaxf(mx0, s[kt][i]), s[kt][i + 1]);
-        mx1 = fmaxf(fmaxf(mx1, s[kt + 1][i]), s[kt + 1][i + 1]);
+          for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(s[kt][8 * h2 + j], c, nm));
+          rs0 += (p[0] + p[1]) + (p[2] + p[3]);
+          rs1 += (p[4] + p[5]) + (p[6] + p[7]);
+          pf[kt][h2] = bf16x8{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3],
+                              (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+        }
+    };
+    using Exact = std::integral_constant<int, kExactMax>;
+    if constexpr (SUMCHECK) {
+      {
+        f32x16 s[NKT];
+        scores(s);
+        if constexpr (FIRST) probs(s, Exact{});
+        else probs(s, std::integral_constant<int, kNoMax>{});
       }
-    const float mx = pair_max(fmaxf(mx0, mx1)) * c;
-    const bool upd = mx > m + kTau;
-    if (__builtin_amdgcn_ballot_w64(upd)) {  // wave-uniform, rare after the first block
-      const float alpha = upd ? fast_exp2(m - mx) : 1.f;
-      if (upd) m = mx;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-    }
-    const float nm = (m == kNegInf) ? 0.f : -m;
-    float rs0 = 0.f, rs1 = 0.f;
-    bf16x8 pf[NKT][2];
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(s[kt][8 * h2 + j], c, nm));
-        rs0 += (p[0] + p[1]) + (p[2] + p[3]);
-        rs1 += (p[4] + p[5]) + (p[6] + p[7]);
-        pf[kt][h2] = bf16x8{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3],
-                            (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+      if (!FIRST && __builtin_amdgcn_ballot_w64(!(rs0 + rs1 <= kSumMax))) {  // rare; also catches +inf
+        // Formed again with the max path, after which every p is at most 1.
+        f32x16 s[NKT];
+        scores(s);
+        probs(s, Exact{});
       }
+    } else {  // the scores and the kLazyMax form written out in place (as lambdas they cost SGPR spills)
+      f32x16 s[NKT];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
+      bf16x8 a[2][NKT];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) a[0][kt] = *(const bf16x8*)(lb + koff[S][0] + kt * 32 * ROWB);
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) {
+        if (kk + 1 < NKS) {
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+            a[(kk + 1) & 1][kt] = *(const bf16x8*)(lb + koff[S][kk + 1] + kt * 32 * ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma_bf16(a[kk & 1][kt], qf[kk], s[kt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
+        const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 4 * hi;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + (i % 4) > lim) s[kt][i] = kNegInf;
+      }
+      float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < NKT; kt += 2)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          mx0 = fmaxf(fmaxf(mx0, s[kt][i]), s[kt][i + 1]);
+          mx1 = fmaxf(fmaxf(mx1, s[kt + 1][i]), s[kt + 1][i + 1]);
+        }
+      const float mx = pair_max(fmaxf(mx0, mx1)) * c;
+      const bool upd = mx > m + kTau;
+      if (__builtin_amdgcn_ballot_w64(upd)) {  // wave-uniform, rare after the first block
+        const float alpha = upd ? fast_exp2(m - mx) : 1.f;
+        if (upd) m = mx;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      }
+      const float nm = (m == kNegInf) ? 0.f : -m;
+      rs0 = 0.f;
+      rs1 = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(s[kt][8 * h2 + j], c, nm));
+          rs0 += (p[0] + p[1]) + (p[2] + p[3]);
+          rs1 += (p[4] + p[5]) + (p[6] + p[7]);
+          pf[kt][h2] = bf16x8{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3],
+                              (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+        }
+    }
     l += pair_sum(rs0 + rs1);
     // O^T += V^T P^T; contraction slots per 16-key step: lanes 0-31 keys
     // {0-3, 8-11}, lanes 32-63 keys {4-7, 12-15} (the accumulator rows).
@@ -270,17 +370,39 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
     }
   };
 
+  using Stage0 = std::integral_constant<int, 0>;
+  using Stage1 = std::integral_constant<int, 1>;
+  using Later = std::false_type;
   issue_loads(0, lds[0]);
-  for (int kb = 0; kb < nkb; kb += 2) {
+  if constexpr (SUMCHECK) {  // key block 0 peeled: it alone forms the max
     wait_vmem();
     __syncthreads();
-    if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
-    compute(kb, std::integral_constant<int, 0>{});
-    if (kb + 1 < nkb) {
+    if (1 < nkb) issue_loads(1, lds[1]);
+    compute(0, Stage0{}, std::true_type{});
+    for (int kb = 1; kb < nkb; kb += 2) {
       wait_vmem();
       __syncthreads();
-      if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
-      compute(kb + 1, std::integral_constant<int, 1>{});
+      if (kb + 1 < nkb) issue_loads(kb + 1, lds[0]);
+      compute(kb, Stage1{}, Later{});
+      if (kb + 1 < nkb) {
+        wait_vmem();
+        __syncthreads();
+        if (kb + 2 < nkb) issue_loads(kb + 2, lds[1]);
+        compute(kb + 1, Stage0{}, Later{});
+      }
+    }
+  } else {
+    for (int kb = 0; kb < nkb; kb += 2) {
+      wait_vmem();
+      __syncthreads();
+      if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
+      compute(kb, Stage0{}, Later{});
+      if (kb + 1 < nkb) {
+        wait_vmem();
+        __syncthreads();
+        if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
+        compute(kb + 1, Stage1{}, Later{});
+      }
     }
   }
 

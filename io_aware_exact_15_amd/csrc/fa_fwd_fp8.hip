@@ -49,10 +49,22 @@ __device__ __forceinline__ int swz8(int r) {
   return (r >> 2) & 3;                                        // 4 chunks per row
 }
 
-// Lazy rescale threshold (log2 units) and the power-of-two scale of P before
-// quantisation: p' = 2^kP8Shift p stays <= 2^(kP8Shift + kTau8) = 256 <= 448.
-constexpr float kTau8 = 3.f;
+// The power-of-two scale of P before quantisation (p' = 2^kP8Shift p keeps
+// small probabilities out of E4M3's subnormals longer) and the bound on a
+// lane's sum of p' over a block, which bounds every p' of it (all are
+// non-negative) below E4M3's largest value, 448.
+//
+// Lazy rescale: the running max m only guards the exponentials (l and the
+// accumulator share it, so O and lse do not depend on its value). It is
+// formed from the scores on key block 0, which every row sees, so every row's
+// max gives p = 1 there and l >= 1 from then on (later probabilities that
+// underflow are negligible against it). Later blocks take p with the m
+// already held and check the lane's sum of p' against kSumMax8; a block that
+// exceeds it (or overflows) is formed again with the max path. For N(0,1)
+// data that sum averages ~150, so the retry is rare, and the row max of every
+// later block is saved: this kernel is bound by its vector work.
 constexpr float kP8Shift = 5.f;
+constexpr float kSumMax8 = 384.f;
 
 // 4 waves x 32 query rows (BR = 128), blocks of BC = 64 keys, three
 // workgroups per CU (151 registers: three waves per SIMD, whose barriers are
@@ -142,62 +154,83 @@ __global__ __launch_bounds__(256, 3) void fwd_fp8_kernel(const uint8_t* __restri
   const int q_last = min(N - 1, qb * BR + BR - 1);
   const int nkb = CAUSAL ? min(nkb_all, q_last / BC + 1) : nkb_all;
 
-  auto compute = [&](int kb, const char* st) {
+  enum { kNoMax, kExactMax };
+  // FIRST: key block 0 (every row of the wave sees at least key 0 of it).
+  auto compute = [&](int kb, const char* st, auto first) {
+    constexpr bool FIRST = decltype(first)::value;
     const int k0 = kb * BC;
-    if (CAUSAL && k0 > qw + 31) return;
+    if (CAUSAL && !FIRST && k0 > qw + 31) return;
     const char* ks = st;
     const char* vs = st + TILEB;
-    f32x16 s[NKT];
+    auto scores = [&](f32x16 (&s)[NKT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      s[kt] = f32x16{};
+      for (int kt = 0; kt < NKT; ++kt) {
+        s[kt] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) {
-        const i32x4 a0 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][0]);
-        const i32x4 a1 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][1]);
-        const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        s[kt] = mfma_f8<FMT, FMT>(a, qf[kk], s[kt]);
+        for (int kk = 0; kk < NKS; ++kk) {
+          const i32x4 a0 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][0]);
+          const i32x4 a1 = *(const i32x4*)(ks + 32 * kt * ROWB + koff[kk][1]);
+          const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          s[kt] = mfma_f8<FMT, FMT>(a, qf[kk], s[kt]);
+        }
       }
-    }
-    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
-      // register i of tile kt holds key k0 + 32 kt + (i & 7) + 8 hi + 16 (i >> 3)
-      const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 8 * hi;
+      if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw)) {
+        // register i of tile kt holds key k0 + 32 kt + (i & 7) + 8 hi + 16 (i >> 3)
+        const int lim = min(CAUSAL ? q : N - 1, N - 1) - k0 - 8 * hi;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + (i & 7) + 16 * (i >> 3) > lim) s[kt][i] = kNegInf;
+      }
+    };
+    float rs0, rs1;
+    // p' = 2^kP8Shift p replaces the scores in s.
+    auto probs = [&](f32x16 (&s)[NKT], auto mode) __attribute__((always_inline)) {
+      if constexpr (decltype(mode)::value == kExactMax) {
+        float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < NKT; kt += 2)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            mx0 = fmaxf(fmaxf(mx0, s[kt][i]), s[kt][i + 1]);
+            mx1 = fmaxf(fmaxf(mx1, s[kt + 1][i]), s[kt + 1][i + 1]);
+          }
+        const float mx = pair_max(fmaxf(mx0, mx1)) * c;
+        const bool upd = mx > m;
+        if (__builtin_amdgcn_ballot_w64(upd)) {
+          const float alpha = upd ? fast_exp2(m - mx) : 1.f;  // 0 while m is still -inf (l, acc are 0)
+          if (upd) m = mx;
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        }
+      }
+      const float shift = kP8Shift - ((m == kNegInf) ? 0.f : m);
+      rs0 = 0.f;
+      rs1 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kt + (i & 7) + 16 * (i >> 3) > lim) s[kt][i] = kNegInf;
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kt][i], c, shift));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kt][i + 1], c, shift));
+          s[kt][i] = p0;
+          s[kt][i + 1] = p1;
+          rs0 += p0;
+          rs1 += p1;
+        }
+    };
+    using Exact = std::integral_constant<int, kExactMax>;
+    f32x16 s[NKT];
+    scores(s);
+    if constexpr (FIRST) probs(s, Exact{});
+    else probs(s, std::integral_constant<int, kNoMax>{});
+    if (!FIRST && __builtin_amdgcn_ballot_w64(!(rs0 + rs1 <= kSumMax8))) {  // rare; also catches +inf
+      // Formed again with the max path, after which every p' is at most 2^kP8Shift.
+      scores(s);
+      probs(s, Exact{});
     }
-    float mx0 = kNegInf, mx1 = kNegInf;
-#pragma unroll
-    for (int kt = 0; kt < NKT; kt += 2)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        mx0 = fmaxf(fmaxf(mx0, s[kt][i]), s[kt][i + 1]);
-        mx1 = fmaxf(fmaxf(mx1, s[kt + 1][i]), s[kt + 1][i + 1]);
-      }
-    const float mx = pair_max(fmaxf(mx0, mx1)) * c;
-    const bool upd = mx > m + kTau8;
-    if (__builtin_amdgcn_ballot_w64(upd)) {
-      const float alpha = upd ? fast_exp2(m - mx) : 1.f;
-      if (upd) m = mx;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-    }
-    const float shift = kP8Shift - ((m == kNegInf) ? 0.f : m);  // p' = 2^kP8Shift p
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[kt][i], c, shift));
-        const float p1 = fast_exp2(__builtin_fmaf(s[kt][i + 1], c, shift));
-        s[kt][i] = p0;
-        s[kt][i + 1] = p1;
-        rs0 += p0;
-        rs1 += p1;
-      }
     l += pair_sum(rs0 + rs1);
     // O^T += V^T P^T, 64-key steps; byte j of step u: tile 2u + j / 16, register j % 16.
 #pragma unroll
@@ -223,16 +256,20 @@ __global__ __launch_bounds__(256, 3) void fwd_fp8_kernel(const uint8_t* __restri
   };
 
   issue_loads(0, lds[0]);
-  for (int kb = 0; kb < nkb; kb += 2) {
+  wait_vmem();
+  __syncthreads();
+  if (1 < nkb) issue_loads(1, lds[1]);
+  compute(0, lds[0], std::true_type{});  // key block 0 peeled: it alone forms the max
+  for (int kb = 1; kb < nkb; kb += 2) {
     wait_vmem();
     __syncthreads();
-    if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
-    compute(kb, lds[0]);
+    if (kb + 1 < nkb) issue_loads(kb + 1, lds[0]);
+    compute(kb, lds[1], std::false_type{});
     if (kb + 1 < nkb) {
       wait_vmem();
       __syncthreads();
-      if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
-      compute(kb + 1, lds[1]);
+      if (kb + 2 < nkb) issue_loads(kb + 2, lds[1]);
+      compute(kb + 1, lds[0], std::false_type{});
     }
   }
 
