@@ -99,7 +99,7 @@ __device__ __forceinline__ int swz(int r) {
 template <int D, int BC, int NW, int LB, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    OutT* __restrict__ O, float* __restrict__ LSE, int BH, int G, int N, int nqb, float c) {
+    OutT* __restrict__ O, float* __restrict__ LSE, int BH, int G, int N, int nqb, float c, int pass_wgs) {
   constexpr int BR = 32 * NW;
   constexpr int NKT = BC / 32;  // 32-key tiles per block
   constexpr int ROWB = 2 * D;          // bytes per tile row
@@ -110,8 +110,19 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   static_assert(NI >= 1 && CPR % NW == 0, "tile load split");
   __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
 
+  // pass_wgs > 0: the whole grid is resident at once, in passes of one
+  // workgroup per CU (pass_wgs = the CU count). Workgroups are then placed
+  // when the grid starts, not as CUs free up, so heaviest-first order alone
+  // would give a CU the heaviest block of every pass. Odd passes run in
+  // reverse order within each XCD (workgroup w goes to XCD w mod 8, which
+  // the reversal keeps), pairing heavy blocks with light ones on each CU.
+  int bid = blockIdx.x;
+  if (pass_wgs > 0) {
+    const int r = bid / pass_wgs, i = bid - r * pass_wgs;
+    if (r & 1) bid = r * pass_wgs + 8 * (pass_wgs / 8 - 1 - (i >> 3)) + (i & 7);
+  }
   int bh, qb;
-  map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
+  map_head_block(bid, BH, G, nqb, false, bh, qb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, col = lane & 31;
   const size_t hoff = (size_t)bh * N * D;         // query head
@@ -525,13 +536,29 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
 // ---------------------------------------------------------------------------
 // Host-side launch selection.
 
+// Compute units of the current device (0 if the runtime cannot say).
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                               int G, int N, float c, hipStream_t st) {
   constexpr int NW = D == 64 ? 4 : 8, BC = D == 64 ? 64 : 128, LB = D == 64 ? 4 : 1;
   const int nqb = (N + 32 * NW - 1) / (32 * NW);
+  const long wgs = (long)BH * nqb;
+  // Causal grids that the CUs hold at once, in two or more whole passes, get
+  // the alternating pass order (unequal blocks, no dynamic balancing).
+  int pass_wgs = 0;
+  if (CAUSAL && LB > 1) {
+    const int cus = cu_count();
+    if (cus > 0 && cus % 8 == 0 && wgs % cus == 0 && wgs / cus >= 2 && wgs <= (long)cus * LB) pass_wgs = cus;
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, LB, CAUSAL, OutT>), dim3(BH * nqb), dim3(64 * NW), 0, st, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, G, N, nqb, c);
+                     (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, G, N, nqb, c, pass_wgs);
   return hipGetLastError();
 }
 

@@ -76,6 +76,15 @@ def test_edge_f32(shape, causal):
     _run_full(B, H, N, d, 200 + N, "f32", causal, o_dtype="f32")
 
 
+@pytest.mark.parametrize("B", [2, 3])
+def test_resident_grid_pass_order(B):
+    """Causal d = 64 grids that the CUs hold at once, in 2 and 3 passes of one
+    workgroup per CU (512 and 768 workgroups on 256 CUs), where odd passes run
+    in reverse order: every element against the oracle (the B = 4 workload
+    covers 4 passes)."""
+    _run_full(B, 16, 2048, 64, 16 + B, "bf16", True)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_operands_f32_output(causal):
     """bf16 operands with a float32 O (the form the backward pass consumes)."""
