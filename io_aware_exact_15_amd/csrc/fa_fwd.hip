@@ -294,7 +294,7 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
         scores(s);
         probs(s, Exact{});
       }
-    } else {  // the scores and the kLazyMax form written out in place (as lambdas they cost SGPR spills)
+    } else {  // the scores and the per-block lazy max written out in place (as lambdas they cost SGPR spills)
       f32x16 s[NKT];
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
@@ -432,20 +432,29 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// float32 operands (P kept in float32), v_mfma_f32_32x32x2_f32. One 32-row
-// query tile per wave, 32 keys per block. K-step i of O^T += V^T P^T pairs
-// accumulator register i of both half-waves, so P needs no conversion.
+// float32 operands (P kept in float32), v_mfma_f32_32x32x2_f32. One
+// workgroup per (batch*head, 32 query rows); its 4 waves split the key blocks
+// of 32 (wave w takes blocks w, w + 4, ...), each keeping its own running
+// max, denominator and output accumulator over its keys, and the 4 partial
+// results are merged through LDS with the combine that the online softmax
+// applies between blocks: m = max m_w, l = sum l_w 2^(m_w - m),
+// O = sum acc_w 2^(m_w - m) / l. At float32 matrix-core rates this path is
+// latency-bound at the sizes it serves, so the split shortens each wave's
+// serial chain fourfold. K-step i of O^T += V^T P^T pairs accumulator
+// register i of both half-waves, so P needs no conversion.
 template <int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
+__global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int BH, int G, int N, int nqb, float c) {
-  constexpr int BR = 128, BC = 32;
-  constexpr int KS = D + 4, VS = D + 4;
+  constexpr int NWV = 4, BC = 32;
+  constexpr int KS = D + 4, VS = D + 4;  // padded rows: conflict-free column reads
   constexpr int KT = BC * KS, VT = BC * VS;
   constexpr int NDT = D / 32;
-  __shared__ __attribute__((aligned(16))) float smem[KT + VT];
-  float* ks = smem;
-  float* vs = smem + KT;
+  // Per wave: its K and V tiles; reused at the end for its partial result
+  // (acc as [d][32 rows], then m[32], l[32]).
+  constexpr int WAVE_FLOATS = KT + VT;
+  static_assert(D * 32 + 64 <= WAVE_FLOATS, "partial result fits in the wave's tiles");
+  __shared__ __attribute__((aligned(16))) float smem[NWV * WAVE_FLOATS];
 
   int bh, qb;
   map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
@@ -453,8 +462,10 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
   const int hi = lane >> 5, col = lane & 31;
   const size_t hoff = (size_t)bh * N * D;         // query head
   const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head
-  const int q0 = qb * BR + wave * 32;
+  const int q0 = qb * 32;
   const int q = q0 + col;
+  float* ks = smem + wave * WAVE_FLOATS;
+  float* vs = ks + KT;
 
   float qf[D / 2];
   {
@@ -468,13 +479,15 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
   float m = kNegInf, l = 0.f;
 
   const int nkb_all = (N + BC - 1) / BC;
-  const int q_last = min(N - 1, qb * BR + BR - 1);
+  const int q_last = min(N - 1, q0 + 31);
   const int nkb = CAUSAL ? min(nkb_all, q_last / BC + 1) : nkb_all;
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  for (int kb = wave; kb < nkb; kb += NWV) {
     const int k0 = kb * BC;
-    __syncthreads();
-    for (int idx = tid; idx < BC * D / 4; idx += 256) {
+    // The wave's own tiles: every earlier read of them has returned (its
+    // values fed the products), so they can be overwritten; the wave-level
+    // fences order these stores before the reads below.
+    for (int idx = lane; idx < BC * D / 4; idx += 64) {
       const int row = idx / (D / 4), c4 = idx % (D / 4), key = k0 + row;
       f32x4 kx = {}, vx = {};
       if (key < N) {
@@ -484,8 +497,9 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
       *(f32x4*)(ks + row * KS + 4 * c4) = kx;
       *(f32x4*)(vs + row * VS + 4 * c4) = vx;
     }
-    __syncthreads();
-    if (CAUSAL && k0 > q0 + 31) continue;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x16 s = {};
 #pragma unroll
     for (int kk = 0; kk < D / 2; ++kk) s = mfma_f32(ks[col * KS + 2 * kk + hi], qf[kk], s);
@@ -520,16 +534,54 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(
       }
     }
   }
-  if (q < N) {
-    const float inv = 1.f / l;
-    OutT* dst = O + hoff + (size_t)q * D + 4 * hi;
+
+  // Merge. Register i of acc[dt] holds dimension 32 dt + 8 (i / 4) + 4 hi + i % 4
+  // of query row col. Each wave stores its partial over its own tiles (its
+  // reads of them have all returned); after the barrier, wave w < NDT
+  // combines dimensions 32 w .. 32 w + 31 of all 32 rows (a wave whose keys
+  // were all masked holds m = -inf and weighs 0).
+  {
+    float* part = ks;  // [d][32 rows], then m[32], l[32]
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        OutStore<OutT>::store4(dst + 32 * dt + 8 * g, acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv,
-                               acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
-    if (hi == 0) LSE[(size_t)bh * N + q] = (m + __log2f(l)) * kLn2;
+      for (int i = 0; i < 16; ++i) part[(32 * dt + 8 * (i / 4) + 4 * hi + (i % 4)) * 32 + col] = acc[dt][i];
+    if (hi == 0) {
+      part[D * 32 + col] = m;
+      part[D * 32 + 32 + col] = l;
+    }
+  }
+  __syncthreads();
+  if (wave < NDT && q < N) {
+    float mw[NWV], M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      mw[w] = smem[w * WAVE_FLOATS + D * 32 + col];
+      M = fmaxf(M, mw[w]);
+    }
+    float fw[NWV], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      fw[w] = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - M);
+      L += smem[w * WAVE_FLOATS + D * 32 + 32 + col] * fw[w];
+    }
+    const float inv = 1.f / L;
+    OutT* dst = O + hoff + (size_t)q * D + 32 * wave;
+    // Lane (hi, col) writes dimensions 32 wave + 16 hi .. + 15 of row col.
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int dd = 32 * wave + 16 * hi + 4 * g + r;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) v += smem[w * WAVE_FLOATS + dd * 32 + col] * fw[w];
+        o4[r] = v * inv;
+      }
+      OutStore<OutT>::store4(dst + 16 * hi + 4 * g, o4[0], o4[1], o4[2], o4[3]);
+    }
+    if (wave == 0 && hi == 0) LSE[(size_t)bh * N + q] = (M + __log2f(L)) * kLn2;
   }
 }
 
@@ -565,7 +617,7 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
 template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                              int G, int N, float c, hipStream_t st) {
-  const int nqb = (N + 127) / 128;
+  const int nqb = (N + 31) / 32;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, OutT>), dim3(BH * nqb), dim3(256), 0, st, (const float*)q,
                      (const float*)k, (const float*)v, (OutT*)o, lse, BH, G, N, nqb, c);
   return hipGetLastError();
