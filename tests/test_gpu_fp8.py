@@ -1,6 +1,7 @@
 """FP8 E4M3 forward parity against the oracle on the dequantised inputs (code * scale)."""
 import numpy as np
 import pytest
+import torch
 
 from io_aware_exact_15_amd import inputs
 from parity import assert_close, assert_lse, gather_rows, gpu_forward, oracle_forward
@@ -37,6 +38,56 @@ def test_edge_fp8(shape, causal):
     mx, rms = assert_close(o, ro, "fp8", "O")
     le = assert_lse(lse, rl, "lse")
     print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+
+
+# Score ranges that move the running max after key block 0 (the FP8 kernel
+# forms the max there only and bounds later blocks by the lane's sum of
+# P' = 2^5 p, forming a block again when the sum passes its bound or
+# overflows): keys from row 300 on scaled by `grow` before quantisation (their
+# scores exceed the earlier ones by up to ~40 and ~260 in log2 units), and
+# queries and keys shifted apart so that every score lies near -260 in log2
+# units. The rows are sharp, so the bound follows from the rounding instead of
+# the flat 6e-2: P' is rounded to E4M3 (4 significant bits, relative error
+# <= 2^-4), O to bf16 (2^-8) and l sums the unrounded p, so
+# |O_gpu - O| <= (2^-4 + 2^-7) sum_j P_j |v_j|, plus 5e-3 for probabilities in
+# E4M3's subnormal range (the oracle gives sum_j P_j |v_j| as its forward
+# with |V|, i.e. the codes with the sign bit cleared). A retry that is
+# missing or wrong misses it by orders of magnitude. lse is bounded by
+# 1e-3 + 2^-13 |lse|: at these score magnitudes (|lse| up to ~100) the FP8
+# matrix-core products are not summed to float32 accuracy (measured: 4.4e-3 at
+# |lse| = 98.6, relative ~2^-14.5, the same with the per-block-max form of the
+# kernel), while for N(0,1) data lse stays within 1e-4.
+FP8_RANGE = [("grow6", 6.0), ("grow40", 40.0), ("shifted", None)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", FP8_RANGE, ids=[c[0] for c in FP8_RANGE])
+def test_score_range_fp8(case, causal):
+    name, grow = case
+    B, H, N, d = 1, 4, 700, 128
+    print(f"case fp8 score range {name} B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+    q, k, v = inputs.normal_tensors(B, H, N, d, 17, 3)
+    if grow is not None:
+        k = k.clone()
+        k[:, :, 300:] *= grow
+    else:
+        q, k = q - 4.0, k + 4.0
+    inp = {}
+    for n, x in zip("qkv", (q, k, v)):
+        inp[n], inp["s" + n] = inputs.quantize_e4m3(x)
+    o, lse = gpu_forward(inp, "fp8", causal)
+    ro, rl = oracle_forward(inp, "fp8", causal)
+    v_abs = (inp["v"].view(torch.uint8) & 0x7F).view(torch.float8_e4m3fn)
+    r_abs, _ = oracle_forward(dict(inp, v=v_abs), "fp8", causal)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    err = np.abs(o - ro)
+    bound = (2.0 ** -4 + 2.0 ** -7) * r_abs + 5e-3
+    worst = float(np.max(err / bound))
+    assert worst <= 1.0, f"O: error {worst:.3g}x the E4M3-P bound (max|err| {err.max():.3g})"
+    lerr = np.abs(lse - rl)
+    lworst = float(np.max(lerr / (1e-3 + 2.0 ** -13 * np.abs(rl))))
+    assert lworst <= 1.0, f"lse: error {lworst:.3g}x its bound (max|err| {lerr.max():.3g})"
+    print(f"  max|dO|={err.max():.3g} ({worst:.2f} of the bound) lse={lerr.max():.3g} ({lworst:.2f} of its bound)", flush=True)
 
 
 def test_workload_fp8_e5m2_causal_n65536_d128_sampled():
