@@ -69,6 +69,15 @@ def test_fwd_edge_bf16(shape, causal):
     _check_fwd(B, H, Hkv, N, d, 600 + N, "bf16", causal)
 
 
+@pytest.mark.parametrize("shape", [(2, 32, 8, 2048, 64), (3, 16, 2, 2048, 64)], ids=["kv8_4passes", "kv2_3passes"])
+def test_fwd_resident_grid_pass_order(shape):
+    """Causal d = 64 grids with grouped heads that the CUs hold at once (1024
+    and 768 workgroups on 256 CUs, four per CU), where odd passes run in
+    reverse order: 512 seeded rows per query head against the oracle."""
+    B, H, Hkv, N, d = shape
+    _check_fwd(B, H, Hkv, N, d, 650 + H, "bf16", True, sample=512)
+
+
 @pytest.mark.parametrize("shape", [(1, 4, 2, 100, 64), (2, 8, 2, 257, 128)], ids=["small", "ragged"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_edge_f32(shape, causal):
