@@ -67,8 +67,9 @@ constexpr float kP8Shift = 5.f;
 constexpr float kSumMax8 = 384.f;
 
 // 4 waves x 32 query rows (BR = 128), blocks of BC = 64 keys, three
-// workgroups per CU (151 registers: three waves per SIMD, whose barriers are
-// independent); K/V tiles HBM -> LDS by DMA into a 2-stage ring of 2 x 16 KB.
+// workgroups per CU (at most 168 registers: three waves per SIMD, whose
+// barriers are independent; at d = 128 three values spill outside the key
+// loop); K/V tiles HBM -> LDS by DMA into a 2-stage ring of 2 x 16 KB.
 // The FP8 products take half the matrix-core time of bf16 ones while the
 // softmax costs the same, so the kernel is bound by vector work, and more
 // waves per SIMD to overlap it measured 1.5-2 % faster than 8 waves with
