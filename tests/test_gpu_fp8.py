@@ -60,25 +60,28 @@ def test_edge_fp8(shape, causal):
 FP8_RANGE = [("grow6", 6.0), ("grow40", 40.0), ("shifted", None)]
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp8e5m2"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("case", FP8_RANGE, ids=[c[0] for c in FP8_RANGE])
-def test_score_range_fp8(case, causal):
+def test_score_range_fp8(case, causal, fmt):
+    """E4M3 and E5M2 inputs (P is E4M3 in both)."""
     name, grow = case
     B, H, N, d = 1, 4, 700, 128
-    print(f"case fp8 score range {name} B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+    print(f"case {fmt} score range {name} B={B} H={H} N={N} d={d} causal={causal}", flush=True)
     q, k, v = inputs.normal_tensors(B, H, N, d, 17, 3)
     if grow is not None:
         k = k.clone()
         k[:, :, 300:] *= grow
     else:
         q, k = q - 4.0, k + 4.0
+    quant = inputs.quantize_e4m3 if fmt == "fp8" else inputs.quantize_e5m2
     inp = {}
     for n, x in zip("qkv", (q, k, v)):
-        inp[n], inp["s" + n] = inputs.quantize_e4m3(x)
-    o, lse = gpu_forward(inp, "fp8", causal)
-    ro, rl = oracle_forward(inp, "fp8", causal)
-    v_abs = (inp["v"].view(torch.uint8) & 0x7F).view(torch.float8_e4m3fn)
-    r_abs, _ = oracle_forward(dict(inp, v=v_abs), "fp8", causal)
+        inp[n], inp["s" + n] = quant(x)
+    o, lse = gpu_forward(inp, fmt, causal)
+    ro, rl = oracle_forward(inp, fmt, causal)
+    v_abs = (inp["v"].view(torch.uint8) & 0x7F).view(inp["v"].dtype)  # sign bit cleared
+    r_abs, _ = oracle_forward(dict(inp, v=v_abs), fmt, causal)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     err = np.abs(o - ro)
     bound = (2.0 ** -4 + 2.0 ** -7) * r_abs + 5e-3
