@@ -83,10 +83,10 @@ template <> struct OutStore<float> {
 //     blocks p is taken with the m already held, and the lane's sum of its p
 //     (which bounds each of them, all being non-negative) is checked against
 //     kSumMax; a block that exceeds it (or overflows) is formed again with the
-//     max path. This saves the row max of every later block; at d = 128 the
-//     check, a branch on all of the block's exponentials, keeps the P.V
-//     products from starting under the last exponentials and costs more than
-//     it saves.
+//     max path. This saves the row max of every later block. At d = 128 the
+//     same form measured slower: with its extra code paths the loop spills
+//     scalar registers, and their reloads cost more vector instructions than
+//     the row max they replace.
 constexpr float kTau = 8.f;
 constexpr float kSumMax = 256.f;
 
