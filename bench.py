@@ -33,7 +33,8 @@ def _flops(B, H, N, d, causal, kind):
 
 
 def _source_sha(names):
-    """sha256 over the kernel sources a measurement depends on."""
+    """sha256 over the kernel sources (and the build script, which holds the
+    compiler flags) that a measurement depends on."""
     import hashlib
     h = hashlib.sha256()
     for n in names:
@@ -42,7 +43,8 @@ def _source_sha(names):
     return h.hexdigest()
 
 
-KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.hpp"], "bwd": ["fa_bwd.hip", "fa_device.hpp"]}
+KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.hpp", "../build.py"],
+                  "bwd": ["fa_bwd.hip", "fa_device.hpp", "../build.py"]}
 TRAFFIC_FILES = {"fwd": "fwd_bf16_causal_b1h32_n16384_d128_traffic.md",
                  "bwd": "bwd_bf16_causal_b1h32_n16384_d128_traffic.md"}
 

@@ -26,6 +26,11 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
+# The backward kernels are scheduled with the compiler's iterative ILP
+# strategy: measured 1.3-1.8 % faster on the causal N=16384 d=128 backward
+# than the default, and no slower on the other backward workloads.
+PER_SOURCE = {"fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
 
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -45,7 +50,7 @@ def build(verbose=False):
         # fmaxf can map to v_max3_f32 without quieting each operand first. The
         # ABI file keeps full IEEE semantics for its argument checks.
         lang = ["-x", "hip", "-fno-honor-nans"] if src.endswith(".hip") else []
-        out = _run([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([HIPCC, *FLAGS, *lang, *PER_SOURCE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj
