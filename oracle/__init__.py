@@ -17,7 +17,7 @@ from .attention import (  # noqa: F401
     backward_gqa,
     forward_decode,
     backward_quantized,
-    online_softmax_chunked,
+    softmax_by_chunks,
     brute_force_forward,
     brute_force_backward,
     decode_e4m3fn,

@@ -56,7 +56,7 @@ __all__ = [
     "scores", "probabilities", "forward", "forward_quantized", "backward",
     "backward_rows", "backward_causal_tail",
     "forward_gqa", "backward_gqa", "forward_decode", "backward_quantized",
-    "online_softmax_chunked", "brute_force_forward", "brute_force_backward",
+    "softmax_by_chunks", "brute_force_forward", "brute_force_backward",
     "decode_e4m3fn", "decode_e5m2",
 ]
 
@@ -353,39 +353,51 @@ def backward_quantized(qc, kc, vc, doc, sq, sk, sv, sdo, scale, causal, fmt_in="
     return backward_gqa(q, k, v, do, scale, causal)
 
 
-def online_softmax_chunked(s_row, v_rows, bounds):
-    """Streaming softmax of one score row over chunks, with values.
+def softmax_by_chunks(s_row, v_rows, bounds):
+    """Softmax-weighted sum of one score row, assembled chunk by chunk.
 
-    The pages' chunked online softmax ([FAQ-mcq] code figure) keeps a
-    running max m and denominator l and rescales them by exp(m - m_new) per
-    chunk; its value numerator is left as a comment there, and is completed
-    here the way [Blog] states it: the running output accumulator O is
-    rescaled by the same factor and the chunk's exp(s - m_new) * v terms are
-    added; after the last chunk O / l is the softmax-weighted output ([Card]
-    definition paragraph: normalise by 1/l at the end).
+    Each chunk of keys bounds[c] .. bounds[c+1]-1 is summarised on its own:
+    its largest score M_c, its exponential sum L_c = sum_j exp(s_j - M_c) and
+    its weighted values A_c = sum_j exp(s_j - M_c) v_j. Two summaries become
+    the summary of their union once both are re-expressed against the larger
+    of the two maxima M: L = L_a exp(M_a - M) + L_b exp(M_b - M), and A the
+    same way. Folding the chunks in one after the other is the pages' running
+    max / running denominator / rescaled output with its exp(m - m_new)
+    correction ([Card] definition paragraph; [Blog] explainer paragraph; the
+    code figure of [FAQ-mcq] keeps only m and l), and the final A / L is the
+    softmax-weighted output ([Card]: normalise by 1/l at the end).
+    A chunk whose scores are all -inf has the empty summary (M = -inf,
+    L = 0, A = 0) and leaves the others unchanged: the reading that such a
+    chunk holds no mass (the figure's exp(m - m_new) would form -inf + inf).
 
     s_row: [n] scores (may hold -inf for masked keys); v_rows: [n, d];
     bounds: chunk edges 0 = b0 < b1 < ... < bK = n.
-    A chunk whose scores are all -inf while m is still -inf contributes
-    nothing (the figure's exp(m - m_new) would be exp(-inf + inf)); that
-    guard is the plain reading that such a chunk holds no mass.
-    Returns (m, l, O / l).
+    Returns (M, L, A / L) of the whole row.
     """
     s_row = _f64(s_row)
     v_rows = _f64(v_rows)
-    m = -math.inf
-    l = 0.0
-    acc = np.zeros(v_rows.shape[1])
+    width = v_rows.shape[1]
+
+    def summary(lo, hi):
+        part = s_row[lo:hi]
+        top = float(np.max(part))
+        if top == -math.inf:
+            return -math.inf, 0.0, np.zeros(width)
+        w = np.exp(part - top)
+        return top, float(np.sum(w)), w @ v_rows[lo:hi]
+
+    def union(a, b):
+        (ma, la, xa), (mb, lb, xb) = a, b
+        top = max(ma, mb)
+        if top == -math.inf:
+            return a
+        fa, fb = math.exp(ma - top), math.exp(mb - top)
+        return top, la * fa + lb * fb, xa * fa + xb * fb
+
+    total = (-math.inf, 0.0, np.zeros(width))
     for lo, hi in zip(bounds[:-1], bounds[1:]):
-        chunk = s_row[lo:hi]
-        m_new = max(m, float(np.max(chunk)))
-        if m_new == -math.inf:
-            continue
-        corr = math.exp(m - m_new)
-        w = np.exp(chunk - m_new)
-        l = l * corr + float(np.sum(w))
-        acc = acc * corr + w @ v_rows[lo:hi]
-        m = m_new
+        total = union(total, summary(lo, hi))
+    m, l, acc = total
     return m, l, acc / l
 
 

@@ -81,7 +81,7 @@ def pin_chunked_equals_full(o):
             splits.append([0] + cut + [n])
             splits.append([0, n])
             for b in splits:
-                m, l, out = o.online_softmax_chunked(s, v, b)
+                m, l, out = o.softmax_by_chunks(s, v, b)
                 assert abs(m - ref_m) <= 1e-12, (n, b)
                 assert abs(l - ref_l) <= 1e-12 * max(1.0, ref_l), (n, b, l, ref_l)
                 assert np.max(np.abs(out - ref_o)) <= 1e-12, (n, b)
@@ -244,8 +244,8 @@ def pin_masked_chunk(o):
     v = g.standard_normal((12, 2))
     s_masked = np.concatenate([np.full(4, -np.inf), s, np.full(4, -np.inf)])
     v_masked = np.concatenate([g.standard_normal((4, 2)), v, g.standard_normal((4, 2))])
-    m, l, out = o.online_softmax_chunked(s, v, [0, 6, 12])
-    m2, l2, out2 = o.online_softmax_chunked(s_masked, v_masked, [0, 4, 10, 16, 20])
+    m, l, out = o.softmax_by_chunks(s, v, [0, 6, 12])
+    m2, l2, out2 = o.softmax_by_chunks(s_masked, v_masked, [0, 4, 10, 16, 20])
     assert m == m2 and abs(l - l2) <= 1e-13 * l and np.max(np.abs(out - out2)) <= 1e-13
 
 

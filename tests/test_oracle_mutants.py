@@ -31,8 +31,9 @@ MUTANTS = {
     "dk_scale_dropped": ("dk[b, h] = c * (ds.T @ q[b, h])", "dk[b, h] = (ds.T @ q[b, h])"),
     "dq_uses_q": ("dq[b, h] = c * (ds @ k[b, h])", "dq[b, h] = c * (ds @ q[b, h])"),
     "dp_sign": ("dp = do[b, h] @ v[b, h].T", "dp = -(do[b, h] @ v[b, h].T)"),
-    "online_no_rescale": ("acc = acc * corr + w @ v_rows[lo:hi]", "acc = acc + w @ v_rows[lo:hi]"),
-    "online_l_no_rescale": ("l = l * corr + float(np.sum(w))", "l = l + float(np.sum(w))"),
+    "chunks_no_rescale": ("xa * fa + xb * fb", "xa + xb"),
+    "chunks_l_no_rescale": ("la * fa + lb * fb", "la + lb"),
+    "chunks_earlier_not_rescaled": ("xa * fa + xb * fb", "xa + xb * fb"),
     "e4m3_bias8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
     "e4m3_subnormal": ("sub = sign * mant * 2.0 ** -9", "sub = sign * mant * 2.0 ** -10"),
     "softmax_no_normalise": ("return e / l, m[:, 0], l[:, 0]", "return e, m[:, 0], l[:, 0]"),
