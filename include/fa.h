@@ -25,8 +25,15 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and is asynchronous. The return value reports argument
  *     validation and launch errors only; a device fault surfaces at the
- *     caller's next synchronisation. On a non-zero return nothing has been
- *     launched and no output has been written.
+ *     caller's next synchronisation.
+ *   - Errors. FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED and FA_ERR_WORKSPACE
+ *     come from validation, before anything is enqueued: nothing has been
+ *     launched and no output has been written. FA_ERR_LAUNCH is the HIP
+ *     runtime refusing one of the call's kernel launches (the status that
+ *     hipLaunchKernel returned for that launch); kernels of the same call
+ *     enqueued before it still run, and the outputs are then unspecified.
+ *     An error left by the caller's own earlier HIP calls is neither
+ *     reported nor cleared.
  *   - Supported head sizes: d = 64 or d = 128. Any N >= 1 (ragged tails are
  *     masked). B = 0 or H = 0 is a no-op that returns FA_OK.
  *   - causal != 0 applies the lower-triangular mask: key j is visible to

@@ -128,9 +128,13 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
   return fa::decode_workspace_bytes(B, H, Hkv, Nq, Nk, d);
 }
 
-int fa_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* workspace,
-              size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode entry points (workspace aside).
+int check_decode(const void* q, const void* k, const void* v, const void* o, int o_dtype, const float* lse, int B,
+                 int H, int Hkv, int Nq, int Nk, int d, float scale) {
   if (B < 0 || H < 0 || Nq < 1 || Nk < Nq) return FA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (Hkv < 1 || (H > 0 && (Hkv > H || H % Hkv != 0))) return FA_ERR_INVALID_ARG;
@@ -144,6 +148,18 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, int o_dtype,
   if ((long long)B * H == 0) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* workspace,
+              size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+              void* stream) {
+  const int st = check_decode(q, k, v, o, o_dtype, lse, B, H, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK || (long long)B * H == 0) return st;
   if (!workspace || workspace_bytes < fa_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d) || !aligned16(workspace))
     return FA_ERR_WORKSPACE;
   return fa::launch_decode(q, k, v, o, o_dtype, lse, workspace, B, H, Hkv, Nq, Nk, d, scale, causal,

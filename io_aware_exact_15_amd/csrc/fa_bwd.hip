@@ -654,23 +654,24 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restr
 }
 
 template <int D, typename OT, int FIN, int FDO>
-static void launch_prep(const void* q, const void* k, const void* v, const void* dO, const void* o, const float* lse,
-                        const float* desc, const BwdWs& ws, long rows, long kv_rows, hipStream_t st) {
+static hipError_t launch_prep(const void* q, const void* k, const void* v, const void* dO, const void* o,
+                              const float* lse, const float* desc, const BwdWs& ws, long rows, long kv_rows,
+                              hipStream_t st) {
   const long threads = rows * (D / 8);
   const int blocks = (int)((threads + 255) / 256);
-  hipLaunchKernelGGL((bwd_prep_kernel<D, OT, FIN, FDO>), dim3(blocks), dim3(256), 0, st, q, k, v, dO, (const OT*)o,
-                     lse, desc, ws, rows, kv_rows);
+  return launch_kernel(bwd_prep_kernel<D, OT, FIN, FDO>, dim3(blocks), dim3(256), st, q, k, v, dO, (const OT*)o, lse,
+                       desc, ws, rows, kv_rows);
 }
 
 template <int D, typename OT>
-static void launch_prep_fmt(int fin, int fdo, const void* q, const void* k, const void* v, const void* dO,
-                            const void* o, const float* lse, const float* desc, const BwdWs& ws, long rows,
-                            long kv_rows, hipStream_t st) {
-  if (fin == 0) launch_prep<D, OT, 0, 0>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
-  else if (fin == 1 && fdo == 2) launch_prep<D, OT, 1, 2>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
-  else if (fin == 1) launch_prep<D, OT, 1, 1>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
-  else if (fdo == 2) launch_prep<D, OT, 2, 2>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
-  else launch_prep<D, OT, 2, 1>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+static hipError_t launch_prep_fmt(int fin, int fdo, const void* q, const void* k, const void* v, const void* dO,
+                                  const void* o, const float* lse, const float* desc, const BwdWs& ws, long rows,
+                                  long kv_rows, hipStream_t st) {
+  if (fin == 0) return launch_prep<D, OT, 0, 0>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  if (fin == 1 && fdo == 2) return launch_prep<D, OT, 1, 2>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  if (fin == 1) return launch_prep<D, OT, 1, 1>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  if (fdo == 2) return launch_prep<D, OT, 2, 2>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
+  return launch_prep<D, OT, 2, 1>(q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
 }
 
 template <int D, bool CAUSAL, bool SCALED>
@@ -679,32 +680,30 @@ static hipError_t launch_bwd_d(const void* q, const void* k, const void* v, cons
                                int N, float scale, int fin, int fdo, const float* desc, hipStream_t st) {
   const long rows = (long)BH * N, kv_rows = rows / G;
   const BwdWs ws = carve_ws(workspace, (size_t)rows, (size_t)kv_rows, D);
-  if (o_dtype == FA_F32)
-    launch_prep_fmt<D, float>(fin, fdo, q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
-  else
-    launch_prep_fmt<D, bf16>(fin, fdo, q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
-  hipError_t e = hipGetLastError();
+  hipError_t e = o_dtype == FA_F32
+                     ? launch_prep_fmt<D, float>(fin, fdo, q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st)
+                     : launch_prep_fmt<D, bf16>(fin, fdo, q, k, v, dO, o, lse, desc, ws, rows, kv_rows, st);
   if (e != hipSuccess) return e;
   const float c = scale * kLog2e;
   const int nkb = (N + 127) / 128;
   float* dk_out = G > 1 ? ws.dKp : dk;  // grouped heads: per-query-head results, summed below
   float* dv_out = G > 1 ? ws.dVp : dv;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SCALED>), dim3(BH * nkb), dim3(512), 0, st, ws, dk_out, dv_out, BH,
-                     G, N, nkb, c, scale, desc);
-  e = hipGetLastError();
+  e = launch_kernel(bwd_dkdv_kernel<D, CAUSAL, SCALED>, dim3(BH * nkb), dim3(512), st, ws, dk_out, dv_out, BH, G, N,
+                    nkb, c, scale, desc);
   if (e != hipSuccess) return e;
   if (G > 1) {
     const long head_elems = (long)N * D, total4 = kv_rows * D / 4;
     const int blocks = (int)((total4 + 255) / 256);
-    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(blocks), dim3(256), 0, st, ws.dKp, dk, head_elems, G, total4);
-    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(blocks), dim3(256), 0, st, ws.dVp, dv, head_elems, G, total4);
-    e = hipGetLastError();
+    e = launch_kernel(bwd_group_sum_kernel, dim3(blocks), dim3(256), st, (const float*)ws.dKp, dk, head_elems, G,
+                      total4);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(bwd_group_sum_kernel, dim3(blocks), dim3(256), st, (const float*)ws.dVp, dv, head_elems, G,
+                      total4);
     if (e != hipSuccess) return e;
   }
   const int nqb = (N + 255) / 256;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SCALED>), dim3(BH * nqb), dim3(512), 0, st, ws, dq, BH, G, N, nqb, c,
-                     scale, desc);
-  return hipGetLastError();
+  return launch_kernel(bwd_dq_kernel<D, CAUSAL, SCALED>, dim3(BH * nqb), dim3(512), st, ws, dq, BH, G, N, nqb, c,
+                       scale, desc);
 }
 
 template <bool SCALED>

@@ -366,19 +366,16 @@ static hipError_t launch_decode_d(const void* q, const void* k, const void* v, v
   const size_t parts_n = (size_t)B * Hkv * nqt * ns;
   const DecodeParts parts = carve_parts(workspace, parts_n, D);
   const int grid = B * Hkv * nqt * ns;
-  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL>), dim3(grid), dim3(256), 0, st, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, parts, H, Hkv, Nq, Nk, nqt, ns, sb, scale * kLog2e);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(decode_split_kernel<D, CAUSAL>, dim3(grid), dim3(256), st, (const bf16*)q,
+                                     (const bf16*)k, (const bf16*)v, parts, H, Hkv, Nq, Nk, nqt, ns, sb, scale * kLog2e);
   if (e != hipSuccess) return e;
   const long rows = (long)B * H * Nq;
   const int mgrid = (int)((rows + 3) / 4);
   if (o_dtype == FA_BF16)
-    hipLaunchKernelGGL((decode_merge_kernel<D, bf16>), dim3(mgrid), dim3(256), 0, st, parts, (bf16*)o, lse, B, H, Hkv,
+    return launch_kernel(decode_merge_kernel<D, bf16>, dim3(mgrid), dim3(256), st, parts, (bf16*)o, lse, B, H, Hkv, Nq,
+                         nqt, ns);
+  return launch_kernel(decode_merge_kernel<D, float>, dim3(mgrid), dim3(256), st, parts, (float*)o, lse, B, H, Hkv,
                        Nq, nqt, ns);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<D, float>), dim3(mgrid), dim3(256), 0, st, parts, (float*)o, lse, B, H,
-                       Hkv, Nq, nqt, ns);
-  return hipGetLastError();
 }
 
 int launch_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* workspace,

@@ -1,14 +1,16 @@
 // Forward pass of exact attention: O = softmax(scale * Q K^T) V and the
 // per-row log-sum-exp, one workgroup per (batch*head, block of query rows).
 //
-// The method: tile Q into row blocks and K, V into column blocks, and for
-// each Q block stream the K/V blocks through on-chip memory while keeping a
-// running row maximum m, a running denominator l and a rescaled output
-// accumulator (the card "FlashAttention Kernel & Online Softmax", definition
-// paragraph; the "FlashAttention" explainer by A. Tiwari). When a block
-// raises the maximum, l and the accumulator are multiplied by exp(m - m_new);
-// one division by l finishes each row. The N x N matrix never leaves
-// registers.
+// The method: each workgroup owns a group of query rows and visits the key
+// and value rows group by group in on-chip memory. Per query row it carries
+// three running quantities, the largest score seen so far m, the sum l of
+// exponentials taken against that maximum, and the matching unnormalised
+// output, and corrects l and the output by exp(m - m_new) whenever a new
+// group raises the maximum, so that no N x N matrix is ever stored (the
+// short-answer page "Walk through what FlashAttention does differently ...",
+// answer paragraph 1; the card "FlashAttention Kernel & Online Softmax",
+// definition paragraph; the "FlashAttention" explainer by A. Tiwari). One
+// division by l finishes each row.
 //
 // gfx950 mapping (per wave of 64 lanes, 32 query rows):
 //   * Scores are formed transposed, S^T = K Q^T, on the matrix cores: the
@@ -609,18 +611,16 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
     const int cus = cu_count();
     if (cus > 0 && cus % 8 == 0 && wgs % cus == 0 && wgs / cus >= 2 && wgs <= (long)cus * LB) pass_wgs = cus;
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, LB, CAUSAL, OutT>), dim3(BH * nqb), dim3(64 * NW), 0, st, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, G, N, nqb, c, pass_wgs);
-  return hipGetLastError();
+  return launch_kernel(fwd_bf16_kernel<D, BC, NW, LB, CAUSAL, OutT>, dim3(BH * nqb), dim3(64 * NW), st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (OutT*)o, lse, BH, G, N, nqb, c, pass_wgs);
 }
 
 template <int D, bool CAUSAL, typename OutT>
 static hipError_t launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                              int G, int N, float c, hipStream_t st) {
   const int nqb = (N + 31) / 32;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, OutT>), dim3(BH * nqb), dim3(256), 0, st, (const float*)q,
-                     (const float*)k, (const float*)v, (OutT*)o, lse, BH, G, N, nqb, c);
-  return hipGetLastError();
+  return launch_kernel(fwd_f32_kernel<D, CAUSAL, OutT>, dim3(BH * nqb), dim3(256), st, (const float*)q,
+                       (const float*)k, (const float*)v, (OutT*)o, lse, BH, G, N, nqb, c);
 }
 
 #define FA_DISPATCH(FN, D, causal, OT, ...)                                        \

@@ -293,9 +293,8 @@ template <int D, bool CAUSAL, int FMT>
 static hipError_t launch_fp8_d(const void* q, const void* k, const void* v, const float* descale, void* o,
                                float* lse, int BH, int G, int N, float scale, hipStream_t st) {
   const int nqb = (N + 127) / 128;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, FMT>), dim3(BH * nqb), dim3(256), 0, st, (const uint8_t*)q,
-                     (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, descale, BH, G, N, nqb, scale);
-  return hipGetLastError();
+  return launch_kernel(fwd_fp8_kernel<D, CAUSAL, FMT>, dim3(BH * nqb), dim3(256), st, (const uint8_t*)q,
+                       (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, descale, BH, G, N, nqb, scale);
 }
 
 template <int FMT>

@@ -4,7 +4,27 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <tuple>
+#include <utility>
+
 namespace fa {
+
+// Enqueues kernel<<<grid, block, 0, stream>>>(args...) through hipLaunchKernel
+// and returns the runtime's status for this launch alone. The calling
+// thread's last-error state is neither read nor cleared, so an error left by
+// the caller's own earlier HIP calls is not reported (or consumed) here.
+template <typename... P, size_t... I>
+hipError_t launch_kernel_impl(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                              std::index_sequence<I...>, std::tuple<P...>& args) {
+  void* argv[] = {static_cast<void*>(&std::get<I>(args))..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
+}
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> conv(std::forward<A>(args)...);
+  return launch_kernel_impl(kernel, grid, block, stream, std::index_sequence_for<P...>{}, conv);
+}
 
 // Forward launch; arguments already validated by the ABI layer. H query
 // heads share Hkv key/value heads (H % Hkv == 0; query head h reads key/value

@@ -210,3 +210,40 @@ def _bwd_typed(**kw):
 ])
 def test_backward_typed_validation(kw, status):
     assert _bwd_typed(**kw) == status
+
+
+@pytest.mark.gpu
+def test_caller_stale_hip_error_is_not_reported_or_consumed():
+    """An error left by the caller's own earlier HIP call (a refused
+    oversized allocation, which launches nothing) must not come back as a
+    launch error of a valid call: each launch reports its own status."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    B, H, N, d = 1, 2, 130, 64
+    q, k, v = (torch.randn(B, H, N, d, device=dev).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(B, H, N, d, dtype=torch.float32, device=dev) for _ in range(3))
+    o32 = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+    hip = ctypes.CDLL(path)  # the runtime this process already uses
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipMalloc.restype = ctypes.c_int
+    hip.hipGetLastError.restype = ctypes.c_int
+    ptr = ctypes.c_void_p()
+    refused = hip.hipMalloc(ctypes.byref(ptr), ctypes.c_size_t(1 << 62))
+    assert refused != 0
+    try:
+        # no torch work between the refused call and these: torch checks the
+        # thread's last error after its own launches
+        fa.fa_forward(q, k, v, o, lse, 1 / 8, True)
+        fa.fa_forward_typed(fa.FA_BF16, fa.FA_F32, q, k, v, None, o32, lse, 1 / 8, True)
+        fa.fa_backward(q, k, v, o32, fa.FA_F32, q, lse, dq, dk, dv, ws, 1 / 8, True)
+    finally:
+        left = hip.hipGetLastError()  # clears the caller's error before torch runs again
+    assert left == refused
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all() and torch.isfinite(o.float()).all()
