@@ -20,7 +20,7 @@ def _run_full(B, H, N, d, seed, dtype, causal, o_dtype="bf16"):
     tol_dtype = "f32" if (dtype == "f32" and o_dtype == "f32") else ("bf16" if dtype != "fp8" else "fp8")
     mx, rms = assert_close(o, ro, tol_dtype, "O", o_bf16=(o_dtype == "bf16"))
     le = assert_lse(lse, rl, "lse")
-    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+    print(f"  max|O err|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
 
 
 def test_workload_f32_n256_d64():
@@ -51,7 +51,7 @@ def test_workload_bf16_causal_n16384_d128_sampled(o_dtype):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     mx, rms = assert_close(gather_rows(o, rows), ro, "bf16", "O", o_bf16=(o_dtype == "bf16"))
     le = assert_lse(gather_rows(lse, rows), rl, "lse")
-    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+    print(f"  max|O err|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
 
 
 # Ragged and small shapes: tails shorter than a tile, a single row, head
@@ -133,7 +133,7 @@ def test_score_range(case, causal, d):
     worst = float(np.max(err / bound))
     assert worst <= 1.0, f"O: error {worst:.3g}x the bf16-P bound (max|err| {err.max():.3g})"
     le = assert_lse(lse, rl, "lse")  # lse reaches ~|180| here; float32 holds it to ~1e-5
-    print(f"  max|dO|={err.max():.3g} ({worst:.2f} of the bound) lse={le:.3g}", flush=True)
+    print(f"  max|O err|={err.max():.3g} ({worst:.2f} of the bound) lse={le:.3g}", flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -203,4 +203,4 @@ def test_plain_entry_point(causal, side_stream):
     ro, rl = oracle_forward(inp, "bf16", causal)
     mx, rms = assert_close(got_o, ro, "bf16", "O", o_bf16=True)
     le = assert_lse(got_l, rl, "lse")
-    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+    print(f"  max|O err|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)

@@ -21,7 +21,7 @@ def test_workload_fp8_causal_n65536_d128_sampled():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     mx, rms = assert_close(gather_rows(o, rows), ro, "fp8", "O")
     le = assert_lse(gather_rows(lse, rows), rl, "lse")
-    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+    print(f"  max|O err|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
 
 
 EDGE = [(1, 1, 1, 128), (1, 1, 33, 64), (1, 2, 200, 128), (2, 3, 129, 64), (1, 8, 1000, 128), (1, 4, 4096, 128)]
@@ -37,7 +37,7 @@ def test_edge_fp8(shape, causal):
     ro, rl = oracle_forward(inp, "fp8", causal)
     mx, rms = assert_close(o, ro, "fp8", "O")
     le = assert_lse(lse, rl, "lse")
-    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+    print(f"  max|O err|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
 
 
 # Score ranges that move the running max after key block 0 (the FP8 kernel
@@ -90,7 +90,7 @@ def test_score_range_fp8(case, causal, fmt):
     lerr = np.abs(lse - rl)
     lworst = float(np.max(lerr / (1e-3 + 2.0 ** -13 * np.abs(rl))))
     assert lworst <= 1.0, f"lse: error {lworst:.3g}x its bound (max|err| {lerr.max():.3g})"
-    print(f"  max|dO|={err.max():.3g} ({worst:.2f} of the bound) lse={lerr.max():.3g} ({lworst:.2f} of its bound)", flush=True)
+    print(f"  max|O err|={err.max():.3g} ({worst:.2f} of the bound) lse={lerr.max():.3g} ({lworst:.2f} of its bound)", flush=True)
 
 
 def test_workload_fp8_e5m2_causal_n65536_d128_sampled():
@@ -105,7 +105,7 @@ def test_workload_fp8_e5m2_causal_n65536_d128_sampled():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     mx, rms = assert_close(gather_rows(o, rows), ro, "fp8e5m2", "O")
     le = assert_lse(gather_rows(lse, rows), rl, "lse")
-    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+    print(f"  max|O err|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=[f"B{b}H{h}N{n}d{d}" for b, h, n, d in EDGE])
@@ -118,4 +118,4 @@ def test_edge_fp8_e5m2(shape, causal):
     ro, rl = oracle_forward(inp, "fp8e5m2", causal)
     mx, rms = assert_close(o, ro, "fp8e5m2", "O")
     le = assert_lse(lse, rl, "lse")
-    print(f"  max|dO|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
+    print(f"  max|O err|={mx:.3g} rms={rms:.3g} lse={le:.3g}", flush=True)
