@@ -58,3 +58,47 @@ def test_cpu_baseline_sample_reports_what_it_timed():
         assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
         assert r["cores"] == len(os.sched_getaffinity(0))
         assert "s wall" in r["sample"]
+
+
+def _tiny_step_outputs(w):
+    """What a correct step of workload w produces, from the oracle (float64)."""
+    import math
+
+    import oracle
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    inp = inputs.make_inputs(B, H, N, d, w["seed"], "bf16", with_do=True)
+    q, k, v, do = (inputs.to_numpy(inp[n]) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.forward(q, k, v, scale, w["causal"])
+    dq, dk, dv = oracle.backward(q, k, v, do, scale, w["causal"])
+    return {"o_bf16": o, "lse_bf16": lse, "o32": o, "lse32": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def test_parity_of_step_accepts_the_exact_result_and_flags_a_wrong_one():
+    w = dict(name="tiny", B=1, H=2, N=96, d=64, causal=True, seed=3)
+    outs = _tiny_step_outputs(w)
+    r = bench.parity_of_step(w, outs, rows_per_head=16, tail=8)
+    assert r["ok"] and max(r[k] for k in bench.PARITY_TOL) < 1e-12
+    for name in ("o32", "dq", "dk", "dv", "lse_bf16"):
+        bad = {n: a.copy() for n, a in outs.items()}
+        if name in ("dk", "dv"):
+            bad[name][0, 1, -1, 3] += 0.02  # a tail key
+        else:
+            bad[name][0, 1] += 0.02  # every row of head 1 (sampled rows included)
+        r = bench.parity_of_step(w, bad, rows_per_head=16, tail=8)
+        assert not r["ok"], name
+
+
+def test_headline_cpu_baseline_times_forward_and_backward():
+    w = dict(name="tiny", B=1, H=4, N=128, d=64, causal=True, seed=3)
+    r = bench.cpu_baseline(w, heads=1)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert "forward + backward of 1 of 4 heads" in r["sample"]
+    assert r["blas"] and r["full_step_extrapolated_s"] > 0
+
+
+def test_workload_table_names_every_workload():
+    t = bench.workload_table()
+    for group in (inputs.WORKLOADS, inputs.GQA_WORKLOADS, inputs.FP8_BWD_WORKLOADS, inputs.DECODE_WORKLOADS,
+                  inputs.FP8_E5M2_WORKLOADS):
+        assert set(group) <= set(t)
