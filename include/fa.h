@@ -21,7 +21,8 @@
  *     aligned; lse and the backward workspace are [B, H, N] float32.
  *   - All tensor pointers are DEVICE pointers owned by the caller. The
  *     library never allocates or frees device memory and keeps no state
- *     between calls.
+ *     between calls, except for the static scratch buffer of
+ *     fa_decode_noalloc (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and is asynchronous. The return value reports argument
  *     validation and launch errors only; a device fault surfaces at the
@@ -54,7 +55,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum  */
   FA_ERR_UNSUPPORTED = -2, /* head size or dtype combination not built   */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  FA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch   */
+  FA_ERR_LAUNCH = -4,      /* the HIP runtime rejected a kernel launch   */
+  FA_ERR_TOO_LARGE = -5    /* fa_decode_noalloc: scratch would not fit   */
 } fa_status;
 
 typedef enum {
@@ -220,6 +222,32 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
 int fa_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
               void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d,
               float scale, int causal, void* stream);
+
+/* Bytes of the static scratch buffer behind fa_decode_noalloc. */
+#define FA_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)(16u << 20) + (size_t)(256u << 10))
+
+/*
+ * fa_decode_noalloc -- fa_decode without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. It allocates nothing: the
+ * split partials live in a file-scope device array of the library,
+ * FA_DECODE_NOALLOC_MAX_WORKSPACE bytes per GPU, held until the process
+ * ends. Arguments, layouts, results and the other errors are those of
+ * fa_decode; the caller still passes q, k, v, o and lse.
+ *   - Returns FA_ERR_TOO_LARGE, before launching anything, when
+ *     fa_decode_workspace_bytes() of the sizes exceeds
+ *     FA_DECODE_NOALLOC_MAX_WORKSPACE (about 1000 partials of 32 rows at
+ *     d = 128: B * Hkv * ceil(G * Nq / 32) * splits); use fa_decode then.
+ *   - The buffer of the current device is used (the device the stream
+ *     belongs to must be current). Its address is looked up on the first
+ *     call on each device.
+ *   - Every call on one GPU shares that GPU's buffer: calls that overlap in
+ *     time on one GPU (other streams, other host threads) race and must be
+ *     serialised by the caller. Nothing in the buffer has to start at zero.
+ */
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+                      int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_string(int status);

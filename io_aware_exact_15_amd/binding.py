@@ -18,6 +18,9 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_LAUNCH = -4
+FA_ERR_TOO_LARGE = -5
+
+FA_DECODE_NOALLOC_MAX_WORKSPACE = (16 << 20) + (256 << 10)  # include/fa.h
 
 FA_F32 = 0
 FA_BF16 = 1
@@ -29,7 +32,7 @@ _TORCH_DTYPE = {FA_F32: torch.float32, FA_BF16: torch.bfloat16, FA_FP8_E4M3: tor
 
 EXPORTS = ("fa_forward", "fa_forward_typed", "fa_backward", "fa_backward_workspace_bytes", "fa_forward_gqa",
            "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_backward_typed", "fa_decode_workspace_bytes",
-           "fa_decode",
+           "fa_decode", "fa_decode_noalloc",
            "fa_status_string")
 
 
@@ -66,6 +69,8 @@ def lib():
         L.fa_backward_typed.restype = i
         L.fa_decode.argtypes = [vp, vp, vp, vp, i, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
         L.fa_decode.restype = i
+        L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, i, f, i, vp]
+        L.fa_decode_noalloc.restype = i
         L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.fa_decode_workspace_bytes.restype = sz
         L.fa_status_string.argtypes = [i]
@@ -177,6 +182,14 @@ def fa_decode(q, k, v, o, o_dtype, lse, workspace, scale, causal, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype), _ptr(lse), _ptr(workspace), nbytes,
                            B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(stream)), "fa_decode")
+
+
+def fa_decode_noalloc(q, k, v, o, o_dtype, lse, scale, causal, stream=None):
+    """Decode step without a workspace: the partials use the library's static per-GPU buffer."""
+    B, H, Nq, d = _dims(q)
+    Hkv, Nk = _dims(k)[1], _dims(k)[2]
+    _check(lib().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                                   float(scale), int(bool(causal)), _stream(stream)), "fa_decode_noalloc")
 
 
 def fa_status_string(status):

@@ -1,5 +1,6 @@
 // C ABI of the attention library: argument validation, then dispatch to the
-// kernel launchers. No allocation, no state, no exceptions across the ABI.
+// kernel launchers. No allocation and no exceptions across the ABI; the only
+// state is fa_decode_noalloc's per-device scratch address (fa_decode.hip).
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <math.h>
@@ -36,6 +37,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head size or dtype not supported";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: the problem needs more scratch than the library's static buffer holds "
+             "(FA_DECODE_NOALLOC_MAX_WORKSPACE bytes); use fa_decode with a workspace";
     default: return "unknown fa_status";
   }
 }
@@ -164,6 +168,14 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, int o_dtype,
     return FA_ERR_WORKSPACE;
   return fa::launch_decode(q, k, v, o, o_dtype, lse, workspace, B, H, Hkv, Nq, Nk, d, scale, causal,
                            (hipStream_t)stream);
+}
+
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int H,
+                      int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  const int st = check_decode(q, k, v, o, o_dtype, lse, B, H, Hkv, Nq, Nk, d, scale);
+  if (st != FA_OK || (long long)B * H == 0) return st;
+  return fa::launch_decode_noalloc(q, k, v, o, o_dtype, lse, B, H, Hkv, Nq, Nk, d, scale, causal,
+                                   (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -23,6 +23,7 @@
 //                 online softmax uses between blocks: m = max m_p,
 //                 l = sum l_p 2^(m_p - m), O = sum acc_p 2^(m_p - m) / l.
 // Scores are in base 2 (scale * log2 e folded into one multiply).
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -388,6 +389,48 @@ int launch_decode(const void* q, const void* k, const void* v, void* o, int o_dt
     e = causal ? launch_decode_d<128, true>(q, k, v, o, o_dtype, lse, workspace, B, H, Hkv, Nq, Nk, scale, stream)
                : launch_decode_d<128, false>(q, k, v, o, o_dtype, lse, workspace, B, H, Hkv, Nq, Nk, scale, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate. The
+// partial results live in `scratch`, a file-scope device array of fixed size
+// that the library owns: each GPU the library runs on holds its own copy
+// until the process ends. On the host the array's name only stands for the
+// symbol; its device address is looked up once per device (with that device
+// current) and cached, and only that address is handed to kernels. The
+// partials need no clearing (every one of them that the merge reads is
+// written by its split workgroup earlier in the same call), and calls that
+// overlap on one GPU share the array and race.
+static __device__ __align__(256) char scratch[FA_DECODE_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+// Device address of the current GPU's scratch array.
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+int launch_decode_noalloc(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int H,
+                          int Hkv, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
+  if (decode_workspace_bytes(B, H, Hkv, Nq, Nk, d) > sizeof(scratch)) return FA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess || ws == nullptr) return FA_ERR_LAUNCH;
+  return launch_decode(q, k, v, o, o_dtype, lse, ws, B, H, Hkv, Nq, Nk, d, scale, causal, stream);
 }
 
 }  // namespace fa

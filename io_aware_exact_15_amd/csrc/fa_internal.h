@@ -58,6 +58,11 @@ size_t backward_workspace_bytes(size_t q_rows, size_t kv_rows, int d);
 int launch_decode(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, void* workspace,
                   int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
 
+// Decode with the library's static scratch array instead of a caller
+// workspace (FA_ERR_TOO_LARGE when the partials do not fit in it).
+int launch_decode_noalloc(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int H,
+                          int Hkv, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
+
 // Decode workspace: per split and wave, the unnormalised partial output
 // (32 x d float32) and its running max and denominator (2 x 32 float32).
 size_t decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);

@@ -247,3 +247,28 @@ def test_caller_stale_hip_error_is_not_reported_or_consumed():
     assert left == refused
     torch.cuda.synchronize()
     assert torch.isfinite(dq).all() and torch.isfinite(o.float()).all()
+
+
+def test_decode_noalloc_validation_and_size_limit():
+    """Arguments are checked as for fa_decode; a problem whose partials
+    exceed the static buffer is refused with FA_ERR_TOO_LARGE before any
+    device work (so this runs without a GPU)."""
+    L = fa.lib()
+
+    def call(B=1, H=8, Hkv=2, Nq=1, Nk=1000, d=128, o_dtype=fa.FA_BF16, q=16):
+        return L.fa_decode_noalloc(q, 16, 16, 16, o_dtype, 16, B, H, Hkv, Nq, Nk, d, ctypes.c_float(0.1), 1, None)
+
+    assert call(Nq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Nk=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Hkv=3) == fa.FA_ERR_INVALID_ARG
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(q=None) == fa.FA_ERR_INVALID_ARG
+    assert call(B=0) == fa.FA_OK
+    big = dict(B=64, H=64, Hkv=64, Nq=1, Nk=128, d=128)
+    assert fa.fa_decode_workspace_bytes(*(big[x] for x in ("B", "H", "Hkv", "Nq", "Nk", "d"))) > \
+        fa.FA_DECODE_NOALLOC_MAX_WORKSPACE
+    assert call(**big) == fa.FA_ERR_TOO_LARGE
+    assert "FA_ERR_TOO_LARGE" in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
+    h = open(os.path.join(ROOT, "include", "fa.h")).read()
+    m = re.search(r"#define FA_DECODE_NOALLOC_MAX_WORKSPACE \(\(size_t\)\((\d+)u << (\d+)\) \+ \(size_t\)\((\d+)u << (\d+)\)\)", h)
+    assert m and (int(m[1]) << int(m[2])) + (int(m[3]) << int(m[4])) == fa.FA_DECODE_NOALLOC_MAX_WORKSPACE
