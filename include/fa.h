@@ -100,10 +100,11 @@ int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, co
 
 /*
  * fa_backward_workspace_bytes -- device workspace that fa_backward needs:
- * two float32 per row (D_i = sum_t dO_it O_it and -lse_i*log2(e)) and fp16
- * copies of Q, K, V and dO (the matrix-core operands of the backward pass),
- * each region rounded up to 256 bytes. 0 for an empty batch or an
- * unsupported head size.
+ * a 4 KiB control block (work-list counters) and 16 KiB of per-workgroup
+ * magnitude records, two float32 per row (D_i = sum_t dO_it O_it and
+ * -lse_i*log2(e)) and fp16 copies of Q, K, V and dO (the matrix-core
+ * operands of the backward pass), each region rounded up to 256 bytes. 0
+ * for an empty batch or an unsupported head size.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 
@@ -118,13 +119,16 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
  *   workspace   : device buffer of at least fa_backward_workspace_bytes();
  *                 its contents on entry are ignored and on return unspecified.
  * The probabilities are recomputed block by block from Q, K and lse; no
- * N x N buffer exists at any time. The matrix-core operands are fp16: bf16
- * inputs are converted exactly while |x| lies in [2^-14, 65504]; smaller
- * magnitudes keep fp16's subnormal resolution (2^-24). Larger magnitudes in
- * q, k, v or dO are outside the supported range: they overflow to infinity in
- * the fp16 copies, and the gradients come out non-finite rather than silently
- * wrong. The softmax probabilities enter the dV product scaled by 2^15, so
- * they stay in fp16's normal range for any sequence length.
+ * N x N buffer exists at any time. The matrix-core operands are fp16 copies
+ * of q, k, v and dO, each multiplied by a power of two chosen per tensor from
+ * its largest magnitude, and dS is formed in the units of the dO and V
+ * copies; the powers of two are undone in float32 on dq, dk, dv. So any
+ * finite bf16 inputs are supported, gradients of training size (dO near
+ * 1e-6 or far below) included: a tensor keeps its values exactly in its copy
+ * down to 2^-17 of its largest magnitude, and smaller values with fp16's
+ * subnormal resolution relative to that magnitude. The softmax probabilities
+ * enter the dV product scaled by 2^15, so they stay in fp16's normal range
+ * for any sequence length.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o, int o_dtype,
                 const void* dO, const float* lse, float* dq, float* dk, float* dv,

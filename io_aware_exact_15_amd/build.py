@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_decode.hip", "fa_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -26,9 +26,10 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
-# The backward kernels are scheduled with the compiler's iterative ILP
-# strategy: measured 1.3-1.8 % faster on the causal N=16384 d=128 backward
-# than the default, and no slower on the other backward workloads.
+# The dK/dV kernel is scheduled with the compiler's iterative ILP strategy
+# (5 % faster than the default on the persistent kernel at N=16384, d=128);
+# the dQ kernel, in a source of its own, keeps the default, under which it
+# does not spill inside its loop.
 PER_SOURCE = {"fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 

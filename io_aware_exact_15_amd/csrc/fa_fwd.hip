@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
 // Host-side launch selection.
 
 // Compute units of the current device (0 if the runtime cannot say).
-static int cu_count() {
+int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
@@ -608,7 +608,7 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   // the alternating pass order (unequal blocks, no dynamic balancing).
   int pass_wgs = 0;
   if (CAUSAL && LB > 1) {
-    const int cus = cu_count();
+    const int cus = device_cu_count();
     if (cus > 0 && cus % 8 == 0 && wgs % cus == 0 && wgs / cus >= 2 && wgs <= (long)cus * LB) pass_wgs = cus;
   }
   return launch_kernel(fwd_bf16_kernel<D, BC, NW, LB, CAUSAL, OutT>, dim3(BH * nqb), dim3(64 * NW), st, (const bf16*)q,

@@ -26,6 +26,9 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_
   return launch_kernel_impl(kernel, grid, block, stream, std::index_sequence_for<P...>{}, conv);
 }
 
+// Compute units of the current device (0 if the runtime cannot say).
+int device_cu_count();
+
 // Forward launch; arguments already validated by the ABI layer. H query
 // heads share Hkv key/value heads (H % Hkv == 0; query head h reads key/value
 // head h / (H / Hkv)).
@@ -47,6 +50,11 @@ int launch_backward(const void* q, const void* k, const void* v, const void* o, 
                     const void* dO, const float* lse, float* dq, float* dk, float* dv,
                     void* workspace, int B, int H, int Hkv, int N, int d, float scale, int causal,
                     int in_fmt, int do_fmt, const float* desc, hipStream_t stream);
+
+// dQ kernel of the backward pass (fa_bwd_dq.hip), after the dK/dV kernel
+// has chosen the copies' exponents; `grid` persistent workgroups.
+hipError_t launch_bwd_dq(int d, int causal, void* workspace, const float* desc, int fin, int fdo, float* dq, int BH,
+                         int G, int N, float c, float scale, int grid, hipStream_t st);
 
 // Backward workspace: D and -lse*log2(e) (float32 per query row), fp16
 // copies of Q and dO (per query row) and of K and V (per key/value row),

@@ -76,11 +76,14 @@ def _bwd(ws_bytes=None, **kw):
                                 a["causal"], None)
 
 
+CTL = 4096 + 1024 * 4 * 4  # control block, then one 4-float magnitude record per prep workgroup
+
+
 def test_workspace_size():
     rows = 2 * 16 * 4096
-    assert fa.fa_backward_workspace_bytes(2, 16, 4096, 128) == 2 * rows * 4 + 4 * rows * 128 * 2
-    # each of the six regions rounds up to 256 bytes
-    assert fa.fa_backward_workspace_bytes(1, 1, 3, 64) == 2 * 256 + 4 * 512
+    assert fa.fa_backward_workspace_bytes(2, 16, 4096, 128) == CTL + 2 * rows * 4 + 4 * rows * 128 * 2
+    # each of the six row regions rounds up to 256 bytes
+    assert fa.fa_backward_workspace_bytes(1, 1, 3, 64) == CTL + 2 * 256 + 4 * 512
     assert fa.fa_backward_workspace_bytes(0, 1, 3, 64) == 0
     assert fa.fa_backward_workspace_bytes(1, 1, 3, 96) == 0
 
@@ -124,7 +127,7 @@ def test_forward_gqa_validation(kw, status):
 def test_gqa_workspace_size():
     q_rows, kv_rows = 2 * 16 * 4096, 2 * 4 * 4096
     assert fa.fa_backward_gqa_workspace_bytes(2, 16, 4, 4096, 128) == \
-        2 * q_rows * 4 + 2 * q_rows * 128 * 2 + 2 * kv_rows * 128 * 2 + 2 * q_rows * 128 * 4
+        CTL + 2 * q_rows * 4 + 2 * q_rows * 128 * 2 + 2 * kv_rows * 128 * 2 + 2 * q_rows * 128 * 4
     assert fa.fa_backward_gqa_workspace_bytes(2, 16, 16, 4096, 128) == fa.fa_backward_workspace_bytes(2, 16, 4096, 128)
     assert fa.fa_backward_gqa_workspace_bytes(1, 6, 4, 64, 64) == 0  # 4 does not divide 6
     assert fa.fa_backward_gqa_workspace_bytes(1, 6, 0, 64, 64) == 0

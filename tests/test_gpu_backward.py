@@ -85,17 +85,3 @@ def test_bench_size_backward_two_heads():
     do = inp["do"].double().numpy()
     assert np.max(np.abs(dk.sum(axis=2))) <= 1e-1
     assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 1e-1
-
-
-def test_out_of_fp16_range_input_gives_non_finite_gradients():
-    """A bf16 input beyond fp16's range (documented as unsupported in fa.h)
-    makes the gradients non-finite instead of silently wrong; the forward,
-    which works on bf16 directly, stays finite."""
-    inp = inputs.make_inputs(1, 2, 200, 64, 31, "bf16", with_do=True)
-    q = inp["q"].clone()
-    q[0, 1, 57, 5] = 1.0e5  # exact in bf16, above fp16's 65504
-    inp = dict(inp, q=q)
-    print("case B=1 H=2 N=200 d=64 seed=31 with q[0,1,57,5]=1e5", flush=True)
-    dq, dk, dv = gpu_backward(inp, True)
-    assert not (np.all(np.isfinite(dq[0, 1])) and np.all(np.isfinite(dk[0, 1])) and np.all(np.isfinite(dv[0, 1])))
-    assert np.all(np.isfinite(dq[0, 0])) and np.all(np.isfinite(dk[0, 0])) and np.all(np.isfinite(dv[0, 0]))
