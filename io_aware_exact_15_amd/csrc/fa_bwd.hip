@@ -235,14 +235,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
   constexpr int NPW = CPR * BQ / 64 / NW;   // 1024-byte DMA instructions per wave per Q (or dO) tile
   constexpr int NPV = CPR * BKV / 64 / NW;  // ... per wave for the V tile
   constexpr int NKS = D / 16, NDT = D / 32;
-  constexpr int NST = 2;
   constexpr int STB = 2 * TILEB + 2 * BQ * 4;  // Q tile, dO tile, NL[BQ], D[BQ]
   static_assert(NPW >= 1 && NPV >= 1, "tile split");
-  static_assert(NST * STB >= 4 * NDT * 16 * 64 * 4, "dK partials fit in the ring");
+  static_assert(STB >= 2 * NDT * 16 * 64 * 4, "dK partials of two key groups fit in a ring stage");
   static_assert(VTB >= 4 * (NDT / 2) * 16 * 64 * 4, "dV partials fit in the K and V tiles");
   __shared__ __attribute__((aligned(1024))) char lds_k[VTB];
   __shared__ __attribute__((aligned(1024))) char lds_v[VTB];
-  __shared__ __attribute__((aligned(1024))) char lds[NST][STB];
+  // Ring stages (Q tile, dO tile, NL, D), one object each (see dma_to_lds).
+  __shared__ __attribute__((aligned(1024))) char lds0[STB];
+  __shared__ __attribute__((aligned(1024))) char lds1[STB];
   __shared__ float s_m[NW][4];
   __shared__ int s_next;
 
@@ -325,39 +326,37 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
     const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head: K, V
     const int k0w = kb * BKV + 32 * kg;             // first key of this wave
     const int key = k0w + col;
-    const i32x4 qr = make_rsrc(w.q + hoff, (unsigned)N * ROWB);
-    const i32x4 orr = make_rsrc(w.dO + hoff, (unsigned)N * ROWB);
-    const i32x4 nlr = make_rsrc(w.NL + (size_t)bh * N, (unsigned)N * 4);
-    const i32x4 dr = make_rsrc(w.Dv + (size_t)bh * N, (unsigned)N * 4);
-    auto issue_loads = [&](int qb, int st) {
+    const rsrc_t qr = buffer_rsrc(w.q + hoff, (unsigned)N * ROWB);
+    const rsrc_t orr = buffer_rsrc(w.dO + hoff, (unsigned)N * ROWB);
+    const rsrc_t nlr = buffer_rsrc(w.NL + (size_t)bh * N, (unsigned)N * 4);
+    const rsrc_t dr = buffer_rsrc(w.Dv + (size_t)bh * N, (unsigned)N * 4);
+    auto issue_loads = [&](int qb, char* st) {
       const unsigned base = (unsigned)qb * TILEB;
-      const unsigned la = lds_addr(lds[st]) + 1024u * NPW * wave_u;
+      char* const la = st + 1024 * NPW * wave_u;
 #pragma unroll
       for (int n = 0; n < NPW; ++n) {
-        load_lds16(qr, la + 1024u * n, base + goff[n]);
-        load_lds16(orr, la + TILEB + 1024u * n, base + goff[n]);
+        dma_to_lds<16>(qr, la + 1024 * n, base + goff[n]);
+        dma_to_lds<16>(orr, la + TILEB + 1024 * n, base + goff[n]);
       }
-      if (row_loader) {
-        const i32x4 r = wave_u == 0 ? nlr : dr;
-        const unsigned dst = lds_addr(lds[st]) + 2 * TILEB + 256u * wave_u;
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                     :
-                     : "s"(dst), "v"((unsigned)(qb * BQ + lane) * 4u), "s"(r)
-                     : "memory", "m0");
+      if (row_loader) {  // waves 0 and 1: NL and D of the block's rows
+        char* const dst = st + 2 * TILEB + 256 * wave_u;
+        const unsigned off = (unsigned)(qb * BQ + lane) * 4u;
+        if (wave_u == 0) dma_to_lds<4>(nlr, dst, off);
+        else dma_to_lds<4>(dr, dst, off);
       }
     };
     // K and V tiles of the item (rows past N read as zeros).
     {
-      const i32x4 kr = make_rsrc(w.k + kvoff, (unsigned)N * ROWB);
-      const i32x4 vr = make_rsrc(w.v + kvoff, (unsigned)N * ROWB);
+      const rsrc_t kr = buffer_rsrc(w.k + kvoff, (unsigned)N * ROWB);
+      const rsrc_t vr = buffer_rsrc(w.v + kvoff, (unsigned)N * ROWB);
       const unsigned base = (unsigned)kb * VTB;
-      const unsigned lk = lds_addr(lds_k) + 1024u * NPV * wave_u;
-      const unsigned lv = lds_addr(lds_v) + 1024u * NPV * wave_u;
+      char* const lk = lds_k + 1024 * NPV * wave_u;
+      char* const lv = lds_v + 1024 * NPV * wave_u;
 #pragma unroll
       for (int n = 0; n < NPV; ++n) {
         const unsigned off = base + dma_off(NPV * wave + n);
-        load_lds16(kr, lk + 1024u * n, off);
-        load_lds16(vr, lv + 1024u * n, off);
+        dma_to_lds<16>(kr, lk + 1024 * n, off);
+        dma_to_lds<16>(vr, lv + 1024 * n, off);
       }
     }
 
@@ -429,22 +428,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
       constexpr bool diag = decltype(diag_c)::value;
       wait_vmem();  // this wave's loads of block qb (and, the first time, of the K/V tiles)
       __syncthreads();
-      if (qb + 1 < nqb) issue_loads(qb + 1, st ^ 1);
+      if (qb + 1 < nqb) issue_loads(qb + 1, st == 0 ? lds1 : lds0);
       const int q0 = qb * BQ + 32 * qh;
       if (diag) {
         // Tiles whose queries all precede the wave's keys add nothing; tiles
         // crossing the diagonal are masked element-wise.
         if (q0 + 31 >= k0w) {
-          if (q0 < k0w + 31) tile(lds[st], q0, std::true_type{});
-          else tile(lds[st], q0, std::false_type{});
+          if (q0 < k0w + 31) tile(st == 0 ? lds0 : lds1, q0, std::true_type{});
+          else tile(st == 0 ? lds0 : lds1, q0, std::false_type{});
         }
       } else {
-        tile(lds[st], q0, std::false_type{});
+        tile(st == 0 ? lds0 : lds1, q0, std::false_type{});
       }
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    issue_loads(qb0, 0);  // qb0 < nqb: the item's keys start before N
+    issue_loads(qb0, lds0);  // qb0 < nqb: the item's keys start before N
     int qb = qb0;
     if (CAUSAL) {
       // the (at most) two query blocks that cross the item's keys
@@ -467,7 +466,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
     // The next item is taken now: the atomic's latency overlaps the exchange.
     int next = -1;
     if (tid == 0) next = pop_item((unsigned*)wsb, 0, total, gridDim.x, xcd);
-    float* red_k = (float*)lds[0];  // [4 key groups][NDT][16][64 lanes]
+    // [4 key groups][NDT][16][64 lanes]: groups 0, 1 in stage 0, 2, 3 in stage 1
+    float* red_k = (float*)(kg < 2 ? lds0 : lds1) + (kg & 1) * NDT * 16 * 64;
     auto red_v = [&](int dt) {      // [4 key groups][NDT / 2][16][64 lanes] in each of the K and V tiles
       return (float*)(dt < NDT / 2 ? lds_k : lds_v) + (kg * (NDT / 2) + dt % (NDT / 2)) * 16 * 64;
     };
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          red_k[((kg * NDT + dt) * 16 + i) * 64 + lane] = dk[dt][i];
+          red_k[(dt * 16 + i) * 64 + lane] = dk[dt][i];
           red_v(dt)[i * 64 + lane] = dv[dt][i];
         }
     }
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kr = k0w + 8 * (i / 4) + 4 * hi + (i % 4);
-          const float vk = (dk[dt][i] + red_k[((kg * NDT + dt) * 16 + i) * 64 + lane]) * fK;
+          const float vk = (dk[dt][i] + red_k[(dt * 16 + i) * 64 + lane]) * fK;
           const float vv = (dv[dt][i] + red_v(dt)[i * 64 + lane]) * fV;
           if (kr < N) {
             dK[hoff + (size_t)kr * D + 32 * dt + col] = vk;

@@ -23,7 +23,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(void* wsb, const float* 
   constexpr int NPW = CPR * BC / 64 / NW;
   constexpr int NKS = D / 16, NDT = D / 32, NKT = BC / 32;
   static_assert(NPW >= 1, "tile split");
-  __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
+  // Ring stages [K | V], one object each (see dma_to_lds).
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILEB];
   __shared__ int s_next;
 
   const unsigned* ctl = (const unsigned*)wsb;  // the workspace starts with the control block
@@ -78,21 +80,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(void* wsb, const float* 
     const size_t kvoff = (size_t)(bh / G) * N * D;  // its key/value head: K, V
     const int qw = qb * BR + 32 * wave_u;           // wave-uniform: the mask test below is a scalar branch
     const int q = qw + col;
-    const i32x4 kr = make_rsrc(w.k + kvoff, (unsigned)N * ROWB);
-    const i32x4 vr = make_rsrc(w.v + kvoff, (unsigned)N * ROWB);
+    const rsrc_t kr = buffer_rsrc(w.k + kvoff, (unsigned)N * ROWB);
+    const rsrc_t vr = buffer_rsrc(w.v + kvoff, (unsigned)N * ROWB);
     auto issue_loads = [&](int kb, char* st) {
       const unsigned base = (unsigned)kb * TILEB;
-      const unsigned la = lds_addr(st) + 1024u * NPW * wave_u;
+      char* const la = st + 1024 * NPW * wave_u;
 #pragma unroll
       for (int n = 0; n < NPW; ++n) {
-        load_lds16(kr, la + 1024u * n, base + goff[n]);
-        load_lds16(vr, la + TILEB + 1024u * n, base + goff[n]);
+        dma_to_lds<16>(kr, la + 1024 * n, base + goff[n]);
+        dma_to_lds<16>(vr, la + TILEB + 1024 * n, base + goff[n]);
       }
     };
 
     // The first K/V block's DMA goes out before the register loads of Q, dO and
     // the row values, so that all of them share one memory round trip.
-    issue_loads(0, lds[0]);
+    issue_loads(0, lds0);
     // Q and dO as B operands: lane holds row q, dims 16 ks + 8 hi + 0..7.
     f16x8 qf[NKS], of[NKS];
     {
@@ -204,13 +206,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(void* wsb, const float* 
     for (int kb = 0; kb < nkb; kb += 2) {
       wait_vmem();
       __syncthreads();
-      if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
-      compute(kb, lds[0]);
+      if (kb + 1 < nkb) issue_loads(kb + 1, lds1);
+      compute(kb, lds0);
       if (kb + 1 < nkb) {
         wait_vmem();
         __syncthreads();
-        if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
-        compute(kb + 1, lds[1]);
+        if (kb + 2 < nkb) issue_loads(kb + 2, lds0);
+        compute(kb + 1, lds1);
       }
     }
 

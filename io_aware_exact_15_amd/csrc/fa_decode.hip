@@ -96,7 +96,9 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
   constexpr int NI = CPR * BC / 64 / NW;  // 1024-byte DMA instructions per wave per tile
   constexpr int NDT = D / 32, NKS = D / 16;
   static_assert(NI >= 1, "tile split");
-  __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
+  // Ring stages [K | V], one object each (see dma_to_lds).
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILEB];
 
   const int G = H / Hkv, R = G * Nq;
   const int s = blockIdx.x % ns, T = blockIdx.x / ns;
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
   const int nblk = (Nk + BC - 1) / BC;
   const int kb0 = s * sb, kb1 = min(nblk, kb0 + sb);
 
-  const i32x4 kr = make_rsrc(K + kvoff, (unsigned)Nk * ROWB);
-  const i32x4 vr = make_rsrc(V + kvoff, (unsigned)Nk * ROWB);
+  const rsrc_t kr = buffer_rsrc(K + kvoff, (unsigned)Nk * ROWB);
+  const rsrc_t vr = buffer_rsrc(V + kvoff, (unsigned)Nk * ROWB);
   unsigned goff[NI];
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
@@ -127,11 +129,11 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
   }
   auto issue_loads = [&](int kb, char* st) __attribute__((always_inline)) {
     const unsigned base = (unsigned)kb * TILEB;
-    const unsigned la = lds_addr(st) + 1024u * NI * wave_u;
+    char* const la = st + 1024 * NI * wave_u;
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      load_lds16(kr, la + 1024u * n, base + goff[n]);
-      load_lds16(vr, la + TILEB + 1024u * n, base + goff[n]);
+      dma_to_lds<16>(kr, la + 1024 * n, base + goff[n]);
+      dma_to_lds<16>(vr, la + TILEB + 1024 * n, base + goff[n]);
     }
   };
 
@@ -225,17 +227,17 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
       }
   };
 
-  if (kb0 < kb1) issue_loads(kb0, lds[0]);
+  if (kb0 < kb1) issue_loads(kb0, lds0);
   for (int kb = kb0; kb < kb1; kb += 2) {
     wait_vmem();
     __syncthreads();
-    if (kb + 1 < kb1) issue_loads(kb + 1, lds[1]);
-    compute(kb, lds[0]);
+    if (kb + 1 < kb1) issue_loads(kb + 1, lds1);
+    compute(kb, lds0);
     if (kb + 1 < kb1) {
       wait_vmem();
       __syncthreads();
-      if (kb + 2 < kb1) issue_loads(kb + 2, lds[0]);
-      compute(kb + 1, lds[1]);
+      if (kb + 2 < kb1) issue_loads(kb + 2, lds0);
+      compute(kb + 1, lds1);
     }
   }
 
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
   // is free once every wave has passed the barrier) into the split's
   // partial: M = max m_w, acc = sum acc_w 2^(m_w - M), l = sum l_w 2^(m_w - M).
   // A column with no visible key in the split keeps m = -inf, l = 0, acc = 0.
-  float* red = (float*)&lds[0][0];  // [waves 1..3][NDT][16][64] acc, then [4][64] m, [4][64] l
+  float* red = (float*)lds0;  // [waves 1..3][NDT][16][64] acc, then [4][64] m, [4][64] l
   float* rm = red + 3 * NDT * 16 * 64;
   float* rl = rm + 4 * 64;
   __syncthreads();

@@ -94,14 +94,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Buffer resource (V#) over [base, base + bytes) as four SGPR words: 48-bit
-// base, stride 0, num_records = bytes, default format word. Buffer loads at
-// offsets past `bytes` return zeros.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
-  const unsigned long long b = (unsigned long long)base;
-  return i32x4{(int)(unsigned)b, (int)((unsigned)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
-}
-
 // Workgroup -> (head bh, block blk). Workgroups are dealt round-robin to the
 // 8 XCDs; every query head of a head group (G consecutive query heads that
 // share one key/value head) and all their blocks land on the same XCD, so a
@@ -130,18 +122,26 @@ __device__ __forceinline__ void map_head_block(int bid, int BH, int G, int nb, b
 // LDS address (byte offset inside the workgroup's LDS) of a __shared__ pointer.
 __device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(size_t)(const FA_LDS void*)p; }
 
-// 16 bytes per lane from buffer byte offset `voff` straight into LDS (LDS DMA):
-// lane l's data lands at lds_base + 16 * l; lds_base must be wave-uniform.
-// Issued as inline asm so that the compiler does not make every later LDS
-// read wait for it: the caller owns the ordering (wait_vmem() then a
-// workgroup barrier before the destination is read, and no DMA into a
-// buffer that another wave may still be reading). M0 is set here and is not
-// relied upon by compiler-generated code in these kernels.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned lds_base, unsigned voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_base), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+// Buffer resource (V#) for the LDS DMA below: 48-bit base, stride 0,
+// num_records = bytes, default format word; buffer loads at offsets past
+// `bytes` return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// BYTES (4 or 16) per lane from buffer byte offset `voff` straight into LDS
+// (LDS DMA): lane l's data lands at dst + BYTES * l; dst must be wave-uniform.
+// The compiler tracks which __shared__ object the load writes: a later read
+// of that object by this wave waits for it, a read of another object does
+// not, so the kernels give each stage of a load ring an object of its own.
+// Other waves' loads into the same stage are ordered by the kernel itself
+// (wait_vmem() by every loading wave, then a workgroup barrier).
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(rsrc_t r, const void* dst, unsigned voff) {
+  static_assert(BYTES == 4 || BYTES == 16, "LDS DMA width");
+  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)dst, 16, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)dst, 4, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -110,7 +110,9 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   constexpr int NI = CPR * BC / 64 / NW;  // load instructions per wave per tile
   constexpr int NDT = D / 32, NKS = D / 16;
   static_assert(NI >= 1 && CPR % NW == 0, "tile load split");
-  __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
+  // Ring stages [K | V], one object each (see dma_to_lds).
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILEB];
 
   // pass_wgs > 0: the whole grid is resident at once, in passes of one
   // workgroup per CU (pass_wgs = the CU count). Workgroups are then placed
@@ -133,8 +135,8 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   const int qw = qb * BR + 32 * wave_u;  // first query row of this wave (wave-uniform: scalar branches below)
   const int q = qw + col;
 
-  const i32x4 kr = make_rsrc(K + kvoff, (unsigned)N * ROWB);
-  const i32x4 vr = make_rsrc(V + kvoff, (unsigned)N * ROWB);
+  const rsrc_t kr = buffer_rsrc(K + kvoff, (unsigned)N * ROWB);
+  const rsrc_t vr = buffer_rsrc(V + kvoff, (unsigned)N * ROWB);
 
   // Load addressing: instruction n of this wave fills tile chunks
   // 64 (NI wave + n) + lane, i.e. row p / CPR, physical chunk p % CPR, which
@@ -147,25 +149,30 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   }
   auto issue_loads = [&](int kb, char* st) {
     const unsigned base = (unsigned)kb * TILEB;
-    const unsigned la = lds_addr(st) + 1024u * NI * wave_u;
+    char* const la = st + 1024 * NI * wave_u;
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      load_lds16(kr, la + 1024u * n, base + goff[n]);
-      load_lds16(vr, la + TILEB + 1024u * n, base + goff[n]);
+      dma_to_lds<16>(kr, la + 1024 * n, base + goff[n]);
+      dma_to_lds<16>(vr, la + TILEB + 1024 * n, base + goff[n]);
     }
   };
 
-  // Read addressing (byte offsets inside a tile).
-  // Offsets are from the start of lds, one set per stage: the second stage
-  // lies beyond the 16-bit immediate offset of LDS reads, and keeping its
-  // bases in registers (hidden from the optimiser, which would otherwise
-  // rebuild them with one vector OR per read) saves that vector work.
+  // Read addressing. The per-lane offsets are held as LDS addresses, one set
+  // per stage (the second stage lies beyond the 16-bit immediate offset of
+  // LDS reads), hidden from the optimiser, which would otherwise rebuild
+  // them with one vector add per read. A read takes the stage object plus
+  // (held address - address of the object): the compiler folds that back
+  // to the held register and still knows which object is read.
+  const int lds_at[2] = {(int)lds_addr(lds0), (int)lds_addr(lds1)};
   int koff[2][NKS];  // K row (32 kt + col), logical chunk 2 kk + hi; + kt * 32 * ROWB
 #pragma unroll
   for (int kk = 0; kk < NKS; ++kk) {
-    koff[0][kk] = col * ROWB + 16 * ((2 * kk + hi) ^ swz<D>(col));
-    koff[1][kk] = koff[0][kk] + 2 * TILEB;
-    asm volatile("" : "+v"(koff[1][kk]));
+    const int o = col * ROWB + 16 * ((2 * kk + hi) ^ swz<D>(col));
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      koff[st][kk] = o + lds_at[st];
+      asm volatile("" : "+v"(koff[st][kk]));
+    }
   }
   int voff[2][NDT][2];  // V row 4 hi + (j >> 2) + 8 sec, byte column 64 dt + 32 g + 8 (j & 3)
   {
@@ -176,9 +183,12 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
       for (int sec = 0; sec < 2; ++sec) {
         const int r = 4 * hi + (j >> 2) + 8 * sec;
         const int bcol = 64 * dt + 32 * g + 8 * (j & 3);
-        voff[0][dt][sec] = TILEB + r * ROWB + 16 * ((bcol >> 4) ^ swz<D>(r)) + (bcol & 15);
-        voff[1][dt][sec] = voff[0][dt][sec] + 2 * TILEB;
-        asm volatile("" : "+v"(voff[1][dt][sec]));
+        const int o = TILEB + r * ROWB + 16 * ((bcol >> 4) ^ swz<D>(r)) + (bcol & 15);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          voff[st][dt][sec] = o + lds_at[st];
+          asm volatile("" : "+v"(voff[st][dt][sec]));
+        }
       }
   }
 
@@ -202,7 +212,6 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   const int q_last = min(N - 1, qb * BR + BR - 1);
   const int nkb = CAUSAL ? min(nkb_all, q_last / BC + 1) : nkb_all;
 
-  const char* const lb = &lds[0][0];
   // SUMCHECK selects the second form of the lazy rescale above. FIRST: key
   // block 0, which every row of the wave sees (at least key 0).
   constexpr bool SUMCHECK = D == 64;
@@ -210,6 +219,7 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   auto compute = [&](int kb, auto stage, auto first) {
     constexpr int S = decltype(stage)::value;
     constexpr bool FIRST = decltype(first)::value;
+    const char* const lb = (S == 0 ? lds0 : lds1) - lds_at[S];  // + a held address: inside the stage object
     const int k0 = kb * BC;
     if (CAUSAL && !FIRST && k0 > qw + 31) return;  // every key of the block is after every query of the wave
     auto scores = [&](f32x16 (&s)[NKT]) __attribute__((always_inline)) {
@@ -386,21 +396,21 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   using Stage0 = std::integral_constant<int, 0>;
   using Stage1 = std::integral_constant<int, 1>;
   using Later = std::false_type;
-  issue_loads(0, lds[0]);
+  issue_loads(0, lds0);
   if constexpr (SUMCHECK) {  // key block 0 peeled: it alone forms the max
     wait_vmem();
     __syncthreads();
-    if (1 < nkb) issue_loads(1, lds[1]);
+    if (1 < nkb) issue_loads(1, lds1);
     compute(0, Stage0{}, std::true_type{});
     for (int kb = 1; kb < nkb; kb += 2) {
       wait_vmem();
       __syncthreads();
-      if (kb + 1 < nkb) issue_loads(kb + 1, lds[0]);
+      if (kb + 1 < nkb) issue_loads(kb + 1, lds0);
       compute(kb, Stage1{}, Later{});
       if (kb + 1 < nkb) {
         wait_vmem();
         __syncthreads();
-        if (kb + 2 < nkb) issue_loads(kb + 2, lds[1]);
+        if (kb + 2 < nkb) issue_loads(kb + 2, lds1);
         compute(kb + 1, Stage0{}, Later{});
       }
     }
@@ -408,12 +418,12 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
     for (int kb = 0; kb < nkb; kb += 2) {
       wait_vmem();
       __syncthreads();
-      if (kb + 1 < nkb) issue_loads(kb + 1, lds[1]);
+      if (kb + 1 < nkb) issue_loads(kb + 1, lds1);
       compute(kb, Stage0{}, Later{});
       if (kb + 1 < nkb) {
         wait_vmem();
         __syncthreads();
-        if (kb + 2 < nkb) issue_loads(kb + 2, lds[0]);
+        if (kb + 2 < nkb) issue_loads(kb + 2, lds0);
         compute(kb + 1, Stage1{}, Later{});
       }
     }

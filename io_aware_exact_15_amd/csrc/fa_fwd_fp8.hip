@@ -84,7 +84,9 @@ __global__ __launch_bounds__(256, 3) void fwd_fp8_kernel(const uint8_t* __restri
   constexpr int NPW = CPR * BC / 64 / NW;  // 1024-byte DMA instructions per wave per tile
   constexpr int NKT = BC / 32, NDT = D / 32, NKS = D / 64, NPV = BC / 64;
   static_assert(NPW >= 1, "tile split");
-  __shared__ __attribute__((aligned(1024))) char lds[2][2 * TILEB];  // [stage][K | V]
+  // Ring stages [K | V], one object each (see dma_to_lds).
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILEB];
 
   int bh, qb;
   map_head_block(blockIdx.x, BH, G, nqb, false, bh, qb);
@@ -98,8 +100,8 @@ __global__ __launch_bounds__(256, 3) void fwd_fp8_kernel(const uint8_t* __restri
   const float s_v = descale[2];
   const float c = scale * descale[0] * descale[1] * kLog2e;
 
-  const i32x4 kr = make_rsrc(K + kvoff, (unsigned)N * ROWB);
-  const i32x4 vr = make_rsrc(V + kvoff, (unsigned)N * ROWB);
+  const rsrc_t kr = buffer_rsrc(K + kvoff, (unsigned)N * ROWB);
+  const rsrc_t vr = buffer_rsrc(V + kvoff, (unsigned)N * ROWB);
   // DMA: instruction n of this wave fills tile chunks 64 (NPW wave + n) + lane,
   // i.e. tile row R = p / CPR, physical chunk p % CPR holding logical chunk
   // (p % CPR) ^ swz8(R). K row R holds key pi(R) (bits 2 and 3 of R swapped);
@@ -114,11 +116,11 @@ __global__ __launch_bounds__(256, 3) void fwd_fp8_kernel(const uint8_t* __restri
   }
   auto issue_loads = [&](int kb, char* st) {
     const unsigned base = (unsigned)kb * TILEB;
-    const unsigned la = lds_addr(st) + 1024u * NPW * wave_u;
+    char* const la = st + 1024 * NPW * wave_u;
 #pragma unroll
     for (int n = 0; n < NPW; ++n) {
-      load_lds16(kr, la + 1024u * n, base + koff_g[n]);
-      load_lds16(vr, la + TILEB + 1024u * n, base + voff_g[n]);
+      dma_to_lds<16>(kr, la + 1024 * n, base + koff_g[n]);
+      dma_to_lds<16>(vr, la + TILEB + 1024 * n, base + voff_g[n]);
     }
   };
   // K operand reads: row 32 kt + col, bytes 64 kk + 32 hi .. + 31 (chunks 4 kk + 2 hi, + 1).
@@ -256,21 +258,21 @@ __global__ __launch_bounds__(256, 3) void fwd_fp8_kernel(const uint8_t* __restri
     }
   };
 
-  issue_loads(0, lds[0]);
+  issue_loads(0, lds0);
   wait_vmem();
   __syncthreads();
-  if (1 < nkb) issue_loads(1, lds[1]);
-  compute(0, lds[0], std::true_type{});  // key block 0 peeled: it alone forms the max
+  if (1 < nkb) issue_loads(1, lds1);
+  compute(0, lds0, std::true_type{});  // key block 0 peeled: it alone forms the max
   for (int kb = 1; kb < nkb; kb += 2) {
     wait_vmem();
     __syncthreads();
-    if (kb + 1 < nkb) issue_loads(kb + 1, lds[0]);
-    compute(kb, lds[1], std::false_type{});
+    if (kb + 1 < nkb) issue_loads(kb + 1, lds0);
+    compute(kb, lds1, std::false_type{});
     if (kb + 1 < nkb) {
       wait_vmem();
       __syncthreads();
-      if (kb + 2 < nkb) issue_loads(kb + 2, lds[1]);
-      compute(kb + 1, lds[0], std::false_type{});
+      if (kb + 2 < nkb) issue_loads(kb + 2, lds1);
+      compute(kb + 1, lds0, std::false_type{});
     }
   }
 
