@@ -44,7 +44,7 @@ def _source_sha(names):
 
 
 KERNEL_SOURCES = {"fwd": ["fa_fwd.hip", "fa_device.hpp", "../build.py"],
-                  "bwd": ["fa_bwd.hip", "fa_device.hpp", "../build.py"]}
+                  "bwd": ["fa_bwd.hip", "fa_bwd_dq.hip", "fa_bwd_common.hpp", "fa_device.hpp", "../build.py"]}
 TRAFFIC_FILES = {"fwd": "fwd_bf16_causal_b1h32_n16384_d128_traffic.md",
                  "bwd": "bwd_bf16_causal_b1h32_n16384_d128_traffic.md"}
 
@@ -246,11 +246,26 @@ def _median_ms(torch, fn, iters, warmup):
     return ts[len(ts) // 2], ts[0]
 
 
-def workload_table():
+# Forward traffic against sequence length: causal bf16 forward, d = 128, the
+# same 524288 query rows (and so the same algorithmic bytes) at every N.
+SWEEP_NS = (2048, 4096, 8192, 16384, 32768, 65536)
+
+
+def sweep_table():
+    return {f"fwd_sweep_bf16_causal_b1h{524288 // n}_n{n}_d128": (
+        "std", dict(B=1, H=524288 // n, Hkv=524288 // n, N=n, d=128, seed=70 + i, dtype="bf16", causal=[True],
+                    backward=False)) for i, n in enumerate(SWEEP_NS)}
+
+
+def workload_table(sweep=False):
     """name -> (kind, workload) for every workload of the path except the
     headline step: "std" (forward, plus backward where it has one), "fp8bwd"
-    (FP8 backward) and "decode"."""
+    (FP8 backward) and "decode"; with `sweep`, the forward traffic sweep
+    instead."""
     from io_aware_exact_15_amd import inputs
+
+    if sweep:
+        return sweep_table()
 
     t = {n: ("std", dict(w, Hkv=w["H"])) for n, w in inputs.WORKLOADS.items()}
     t.update((n, ("std", dict(w, Hkv=w["H"]))) for n, w in inputs.FP8_E5M2_WORKLOADS.items())
@@ -336,12 +351,12 @@ def workload_calls(name, kind, w, dev):
     return inp, calls
 
 
-def run_configs(iters=20, warmup=3, with_cpu=True, only=None):
+def run_configs(iters=20, warmup=3, with_cpu=True, only=None, sweep=False):
     """Times every workload of the path (one JSON line per workload and pass)."""
     import torch
 
     dev = torch.device("cuda:0")
-    for name, (kind, w) in workload_table().items():
+    for name, (kind, w) in workload_table(sweep).items():
         if only and name not in only:
             continue
         inp, calls = workload_calls(name, kind, w, dev)
@@ -372,11 +387,11 @@ def run_configs(iters=20, warmup=3, with_cpu=True, only=None):
                                   "ms_median": fm + med, "tflops": tot, "frac_of_peak": tot / c["peak"]}), flush=True)
 
 
-def run_counters(only):
+def run_counters(only, sweep=False):
     """Untimed, for hardware-counter runs: one float32 copy-kernel launch of
     known size (512 MiB read + 512 MiB written, the traffic calibration),
     then one call of every pass of the named workloads (the headline step
-    when `only` is empty)."""
+    when `only` is empty; every sweep point with `sweep`)."""
     import torch
 
     dev = torch.device("cuda:0")
@@ -385,9 +400,11 @@ def run_counters(only):
     torch.mul(src, 1.0, out=dst)  # copy kernel: reads 512 MiB, writes 512 MiB
     torch.cuda.synchronize()
     del src, dst
+    table = workload_table(sweep)
+    if sweep and not only:
+        only = list(table)
     if not only:
         return False
-    table = workload_table()
     for name in only:
         if name not in table:
             raise SystemExit(f"unknown workload {name}; known: {', '.join(table)}")
@@ -413,6 +430,9 @@ def main():
                     help="time every workload (fwd, and bwd where it has one); one JSON line each")
     ap.add_argument("--only", action="append", default=[],
                     help="with --configs or --counters: only this workload (repeatable)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="with --configs or --counters: the forward traffic sweep (causal bf16, d=128, "
+                         "N = 2048 ... 65536, 524288 query rows each) instead of the workloads")
     ap.add_argument("--counters", action="store_true",
                     help="untimed: one float32 copy-kernel launch of known size (512 MiB read + 512 MiB written, "
                          "the traffic calibration) and one step (or one call of each pass of the --only "
@@ -424,9 +444,9 @@ def main():
         sys.exit(2)
 
     if args.configs:
-        run_configs(with_cpu=not args.no_cpu, only=args.only)
+        run_configs(with_cpu=not args.no_cpu, only=args.only, sweep=args.sweep)
         return
-    if args.counters and run_counters(args.only):
+    if args.counters and run_counters(args.only, args.sweep):
         return
 
     import torch
