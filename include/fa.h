@@ -151,11 +151,13 @@ int fa_forward_gqa(int in_dtype, int o_dtype, const void* q, const void* k, cons
                    float scale, int causal, void* stream);
 
 /*
- * fa_backward_gqa_workspace_bytes -- workspace of fa_backward_gqa: two
- * float32 and fp16 copies of Q and dO per query row, fp16 copies of K and V
- * per key/value row and, when Hkv < H, float32 per-query-head dK and dV
- * (B*H*N*d each), every region rounded up to 256 bytes. 0 for an empty
- * batch, an unsupported head size or an Hkv that does not divide H.
+ * fa_backward_gqa_workspace_bytes -- workspace of fa_backward_gqa: the 4 KiB
+ * control block and 16 KiB of magnitude records (as for fa_backward), two
+ * float32 per query row (D and the exponent offset of P), fp16 copies of Q
+ * and dO per query row, fp16 copies of K and V per key/value row and, when
+ * Hkv < H, float32 per-query-head dK and dV (B*H*N*d each), every region
+ * rounded up to 256 bytes. 0 for an empty batch, an unsupported head size or
+ * an Hkv that does not divide H.
  */
 size_t fa_backward_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
@@ -184,9 +186,11 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
  *   descale : FP8 only: DEVICE pointer to 4 float32 per-tensor scales
  *             {s_q, s_k, s_v, s_dO}; the tensors stand for code * s. Must be
  *             NULL for bf16.
- * The FP8 codes are converted exactly to fp16 matrix-core operands (every
- * E4M3 and E5M2 value is an fp16 value) and the scales are applied in
- * float32: to the score exponent, to dP, and to dQ, dK, dV. Mixing bf16 and
+ * The FP8 codes become fp16 matrix-core operands times a per-tensor power of
+ * two, as bf16 values do in fa_backward (by default 2^-6 for E4M3 and 2^-13
+ * for E5M2, which keeps the largest code below 8), and the scales are
+ * applied in float32: to the score exponent, to dP, and to dQ, dK, dV.
+ * Mixing bf16 and
  * FP8 between the two dtypes returns FA_ERR_UNSUPPORTED. o, lse, dq, dk, dv,
  * the workspace (fa_backward_gqa_workspace_bytes) and every other rule are
  * those of fa_backward_gqa.
