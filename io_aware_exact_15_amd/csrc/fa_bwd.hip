@@ -294,7 +294,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
     // DMA addressing: instruction n of this wave fills tile chunks 64 (NP wave + n) + lane.
     auto dma_off = [&](int n_global) {
       const int p = 64 * n_global + ln, row = p / CPR, pc = p % CPR;
-      return (unsigned)(row * ROWB + 16 * (pc ^ swz_b<D>(row)));
+      return (unsigned)(row * ROWB + 16 * (pc ^ tile_swz<D>(row)));
     };
     unsigned goff[NPW];
 #pragma unroll
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
     // 4 hi + (j >> 2) + 8 sec, byte column 64 dt + 32 g + 8 (j & 3).
     int roff[NKS];
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) roff[kk] = col * ROWB + 16 * ((2 * kk + hi) ^ swz_b<D>(col));
+    for (int kk = 0; kk < NKS; ++kk) roff[kk] = col * ROWB + 16 * ((2 * kk + hi) ^ tile_swz<D>(col));
     int toff[NDT][2];
     {
       const int j = ln & 15, g = (ln >> 4) & 1;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(void* wsb, BwdIn in, f
         for (int sec = 0; sec < 2; ++sec) {
           const int r = 4 * hi + (j >> 2) + 8 * sec;
           const int bcol = 64 * dt + 32 * g + 8 * (j & 3);
-          toff[dt][sec] = r * ROWB + 16 * ((bcol >> 4) ^ swz_b<D>(r)) + (bcol & 15);
+          toff[dt][sec] = r * ROWB + 16 * ((bcol >> 4) ^ tile_swz<D>(r)) + (bcol & 15);
         }
     }
     const char* krow = lds_k + 32 * kg * ROWB;  // this wave's 32 K rows (B operand of S)

@@ -27,19 +27,6 @@ __device__ __forceinline__ s16x4 lds_read_tr16h(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 FA_LDS*)(p));
 }
 
-// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
-// does not wait for this wave's global stores to complete.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-template <int D>
-__device__ __forceinline__ int swz_b(int r) {
-  if (D == 128) return (4 * (r & 3)) ^ ((r >> 2) & 3);
-  return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);
-}
 
 constexpr float kPScale = 15.f;            // P is scaled by 2^kPScale for the dV product
 constexpr float kPScaleInv = 1.f / 32768.f;  // 2^-kPScale

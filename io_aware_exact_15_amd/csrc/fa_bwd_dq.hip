@@ -57,11 +57,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(void* wsb, const float* 
 #pragma unroll
     for (int n = 0; n < NPW; ++n) {
       const int p = 64 * (NPW * wave + n) + ln, row = p / CPR, pc = p % CPR;
-      goff[n] = row * ROWB + 16 * (pc ^ swz_b<D>(row));
+      goff[n] = row * ROWB + 16 * (pc ^ tile_swz<D>(row));
     }
     int roff[NKS];
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) roff[kk] = col * ROWB + 16 * ((2 * kk + hi) ^ swz_b<D>(col));
+    for (int kk = 0; kk < NKS; ++kk) roff[kk] = col * ROWB + 16 * ((2 * kk + hi) ^ tile_swz<D>(col));
     int toff[NDT][2];
     {
       const int j = ln & 15, g = (ln >> 4) & 1;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(void* wsb, const float* 
         for (int sec = 0; sec < 2; ++sec) {
           const int r = 4 * hi + (j >> 2) + 8 * sec;
           const int bcol = 64 * dt + 32 * g + 8 * (j & 3);
-          toff[dt][sec] = r * ROWB + 16 * ((bcol >> 4) ^ swz_b<D>(r)) + (bcol & 15);
+          toff[dt][sec] = r * ROWB + 16 * ((bcol >> 4) ^ tile_swz<D>(r)) + (bcol & 15);
         }
     }
     int bh, qb;

@@ -38,11 +38,6 @@ constexpr int kDecBC = 128;   // keys per block
 constexpr int kDecWaves = 4;  // waves per workgroup (32 keys of each block each)
 constexpr float kDecTau = 8.f;
 
-template <int D>
-__device__ __forceinline__ int swz_d(int r) {
-  if (D == 128) return (4 * (r & 3)) ^ ((r >> 2) & 3);
-  return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);
-}
 
 }  // namespace
 
@@ -125,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
     const int p = 64 * (NI * wave + n) + lane, row = p / CPR, pc = p % CPR;
-    goff[n] = row * ROWB + 16 * (pc ^ swz_d<D>(row));
+    goff[n] = row * ROWB + 16 * (pc ^ tile_swz<D>(row));
   }
   auto issue_loads = [&](int kb, char* st) __attribute__((always_inline)) {
     const unsigned base = (unsigned)kb * TILEB;
@@ -143,7 +138,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
 #pragma unroll
   for (int kk = 0; kk < NKS; ++kk) {
     const int row = 32 * wave + col;
-    koff[kk] = row * ROWB + 16 * ((2 * kk + hi) ^ swz_d<D>(row));
+    koff[kk] = row * ROWB + 16 * ((2 * kk + hi) ^ tile_swz<D>(row));
   }
   int voff[NDT][2];
   {
@@ -154,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const bf16* __rest
       for (int sec = 0; sec < 2; ++sec) {
         const int rr = 32 * wave + 4 * hi + (j >> 2) + 8 * sec;
         const int bcol = 64 * dt + 32 * gg + 8 * (j & 3);
-        voff[dt][sec] = TILEB + rr * ROWB + 16 * ((bcol >> 4) ^ swz_d<D>(rr)) + (bcol & 15);
+        voff[dt][sec] = TILEB + rr * ROWB + 16 * ((bcol >> 4) ^ tile_swz<D>(rr)) + (bcol & 15);
       }
   }
 

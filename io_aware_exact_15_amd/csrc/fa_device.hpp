@@ -144,6 +144,25 @@ __device__ __forceinline__ void dma_to_lds(rsrc_t r, const void* dst, unsigned v
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)dst, 4, voff, 0, 0, 0);
 }
 
+// Tile layout in LDS shared by the bf16/fp16 kernels: rows of D 2-byte
+// elements (D / 8 chunks of 16 bytes), chunk c of row r stored at chunk
+// c ^ tile_swz<D>(r). Reads of 16 rows at one chunk (ds_read_b128) and the
+// transposing reads of 4 rows x 64 bytes (ds_read_b64_tr_b16) then hit
+// distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if (D == 128) return (4 * (r & 3)) ^ ((r >> 2) & 3);  // 16 chunks per row
+  return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);        // 8 chunks per row
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for this wave's global stores to complete.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.

@@ -66,7 +66,7 @@ template <> struct OutStore<float> {
 // K/V tiles go HBM -> LDS with buffer loads that write LDS directly (no
 // staging registers; rows past N come back as zeros) into a 2-stage ring.
 // Tiles are row-major, D*2 bytes per row, with the 16-byte chunks of row r
-// XOR-permuted by swz(r) so that both the row reads of K (ds_read_b128, 16
+// XOR-permuted by tile_swz(r) so that both the row reads of K (ds_read_b128, 16
 // rows at one column) and the transposing reads of V (ds_read_b64_tr_b16, 4
 // rows x 64 bytes) hit distinct LDS banks.
 //
@@ -92,11 +92,6 @@ template <> struct OutStore<float> {
 constexpr float kTau = 8.f;
 constexpr float kSumMax = 256.f;
 
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if (D == 128) return (4 * (r & 3)) ^ ((r >> 2) & 3);  // 16 chunks per row
-  return (4 * ((r >> 1) & 1)) ^ ((r >> 2) & 3);        // 8 chunks per row
-}
 
 template <int D, int BC, int NW, int LB, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
@@ -140,12 +135,12 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
 
   // Load addressing: instruction n of this wave fills tile chunks
   // 64 (NI wave + n) + lane, i.e. row p / CPR, physical chunk p % CPR, which
-  // holds logical chunk (p % CPR) ^ swz(row).
+  // holds logical chunk (p % CPR) ^ tile_swz(row).
   unsigned goff[NI];
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
     const int p = 64 * (NI * wave + n) + lane, row = p / CPR, pc = p % CPR;  // row < BC
-    goff[n] = row * ROWB + 16 * (pc ^ swz<D>(row));
+    goff[n] = row * ROWB + 16 * (pc ^ tile_swz<D>(row));
   }
   auto issue_loads = [&](int kb, char* st) {
     const unsigned base = (unsigned)kb * TILEB;
@@ -167,7 +162,7 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
   int koff[2][NKS];  // K row (32 kt + col), logical chunk 2 kk + hi; + kt * 32 * ROWB
 #pragma unroll
   for (int kk = 0; kk < NKS; ++kk) {
-    const int o = col * ROWB + 16 * ((2 * kk + hi) ^ swz<D>(col));
+    const int o = col * ROWB + 16 * ((2 * kk + hi) ^ tile_swz<D>(col));
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       koff[st][kk] = o + lds_at[st];
@@ -183,7 +178,7 @@ __global__ __launch_bounds__(64 * NW, LB) void fwd_bf16_kernel(
       for (int sec = 0; sec < 2; ++sec) {
         const int r = 4 * hi + (j >> 2) + 8 * sec;
         const int bcol = 64 * dt + 32 * g + 8 * (j & 3);
-        const int o = TILEB + r * ROWB + 16 * ((bcol >> 4) ^ swz<D>(r)) + (bcol & 15);
+        const int o = TILEB + r * ROWB + 16 * ((bcol >> 4) ^ tile_swz<D>(r)) + (bcol & 15);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           voff[st][dt][sec] = o + lds_at[st];
