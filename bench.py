@@ -260,8 +260,8 @@ def sweep_table():
 def workload_table(sweep=False):
     """name -> (kind, workload) for every workload of the path except the
     headline step: "std" (forward, plus backward where it has one), "fp8bwd"
-    (FP8 backward) and "decode"; with `sweep`, the forward traffic sweep
-    instead."""
+    (FP8 backward), "decode" and "ws" (the wave-specialised forward); with
+    `sweep`, the forward traffic sweep instead."""
     from io_aware_exact_15_amd import inputs
 
     if sweep:
@@ -272,6 +272,9 @@ def workload_table(sweep=False):
     t.update((n, ("std", w)) for n, w in inputs.GQA_WORKLOADS.items())
     t.update((n, ("fp8bwd", w)) for n, w in inputs.FP8_BWD_WORKLOADS.items())
     t.update((n, ("decode", w)) for n, w in inputs.DECODE_WORKLOADS.items())
+    # The wave-specialised forward (fa_forward_ws) on the bf16 forward workloads.
+    for n in ("fwd_bf16_causal_b1h32_n16384_d128", "fwd_bf16_b4h16_n2048_d64"):
+        t["ws_" + n] = ("ws", dict(inputs.WORKLOADS[n], Hkv=inputs.WORKLOADS[n]["H"]))
     return t
 
 
@@ -322,6 +325,13 @@ def workload_calls(name, kind, w, dev):
     inp = inputs.make_inputs_heads(B, H, Hkv, N, N, d, w["seed"], w["dtype"], with_do=w["backward"])
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    if kind == "ws":
+        o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev)
+        for causal in w["causal"]:
+            calls.append(dict(pass_="fwd", causal=causal, setup=None, peak=PEAK_BF16_TFLOPS, dtype="bf16",
+                              flop=_flops(B, H, N, d, causal, "fwd"), note="wave-specialised schedule (fa_forward_ws)",
+                              fn=(lambda c=causal: fa.fa_forward_ws(fa.FA_BF16, q, k, v, o, lse, scale, c))))
+        return inp, calls
     desc = None
     if w["dtype"] in ("fp8", "fp8e5m2"):
         in_t = fa.FA_FP8_E4M3 if w["dtype"] == "fp8" else fa.FA_FP8_E5M2

@@ -151,6 +151,28 @@ int fa_forward_gqa(int in_dtype, int o_dtype, const void* q, const void* k, cons
                    float scale, int causal, void* stream);
 
 /*
+ * fa_forward_ws -- the bf16 forward of fa_forward_gqa under a
+ * wave-specialised producer/consumer schedule. In each workgroup, four
+ * consumer waves run every matrix-core product (S = Q K^T and O += P V),
+ * and four producer waves, one beside each consumer on its SIMD, stream the
+ * K and V tiles into on-chip memory and turn scores into probabilities,
+ * handing them over through LDS. This is the warp-specialisation idea that
+ * the card "FlashAttention Kernel & Online Softmax" (history paragraph) and
+ * the FlashAttention-family short-answer page (answer paragraph 2) give for
+ * FlashAttention-3 on Hopper, re-derived for CDNA4; fa_forward's schedule, in
+ * which every wave does both kinds of work, is the faster one on gfx950.
+ *   o_dtype : FA_BF16 or FA_F32 output.
+ *   q       : bf16 [B,H,N,d]; k, v: bf16 [B,Hkv,N,d], Hkv divides H.
+ *   o       : [B,H,N,d] in o_dtype; lse: float32 [B,H,N].
+ * Same operation, layouts, sizes and error rules as fa_forward_gqa with
+ * in_dtype = FA_BF16 and descale = NULL. Results agree with fa_forward to
+ * rounding, not bit for bit: 64-key blocks change where the running max
+ * moves and how the denominator's partial sums group.
+ */
+int fa_forward_ws(int o_dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/*
  * fa_backward_gqa_workspace_bytes -- workspace of fa_backward_gqa: the 4 KiB
  * control block and 16 KiB of magnitude records (as for fa_backward), two
  * float32 per query row (D and the exponent offset of P), fp16 copies of Q

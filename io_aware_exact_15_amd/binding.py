@@ -32,7 +32,7 @@ _TORCH_DTYPE = {FA_F32: torch.float32, FA_BF16: torch.bfloat16, FA_FP8_E4M3: tor
 
 EXPORTS = ("fa_forward", "fa_forward_typed", "fa_backward", "fa_backward_workspace_bytes", "fa_forward_gqa",
            "fa_backward_gqa_workspace_bytes", "fa_backward_gqa", "fa_backward_typed", "fa_decode_workspace_bytes",
-           "fa_decode", "fa_decode_noalloc",
+           "fa_decode", "fa_decode_noalloc", "fa_forward_ws",
            "fa_status_string")
 
 
@@ -73,6 +73,8 @@ def lib():
         L.fa_decode_noalloc.restype = i
         L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.fa_decode_workspace_bytes.restype = sz
+        L.fa_forward_ws.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.fa_forward_ws.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -143,6 +145,14 @@ def fa_forward_gqa(in_dtype, o_dtype, q, k, v, descale, o, lse, scale, causal, s
     _check(lib().fa_forward_gqa(int(in_dtype), int(o_dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(descale),
                                 _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale), int(bool(causal)),
                                 _stream(stream)), "fa_forward_gqa")
+
+
+def fa_forward_ws(o_dtype, q, k, v, o, lse, scale, causal, stream=None):
+    """bf16 forward under the wave-specialised schedule: q, o [B,H,N,d]; k, v [B,Hkv,N,d]."""
+    B, H, N, d = _dims(q)
+    Hkv = _dims(k)[1]
+    _check(lib().fa_forward_ws(int(o_dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                               float(scale), int(bool(causal)), _stream(stream)), "fa_forward_ws")
 
 
 def fa_backward_gqa_workspace_bytes(B, H, Hkv, N, d):

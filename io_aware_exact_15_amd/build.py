@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_decode.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_fwd_ws.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_decode.hip", "fa_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

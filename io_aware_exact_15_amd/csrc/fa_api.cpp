@@ -66,6 +66,18 @@ int fa_forward_gqa(int in_dtype, int o_dtype, const void* q, const void* k, cons
                             (hipStream_t)stream);
 }
 
+int fa_forward_ws(int o_dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int Hkv, int N, int d, float scale, int causal, void* stream) {
+  int st = check_shape(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (Hkv < 1 || (H > 0 && (Hkv > H || H % Hkv != 0))) return FA_ERR_INVALID_ARG;
+  if (o_dtype != FA_F32 && o_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  return fa::launch_forward_ws(o_dtype, q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, (hipStream_t)stream);
+}
+
 int fa_forward_typed(int in_dtype, int o_dtype, const void* q, const void* k, const void* v,
                      const float* descale, void* o, float* lse, int B, int H, int N, int d,
                      float scale, int causal, void* stream) {

@@ -36,6 +36,10 @@ int launch_forward(int in_dtype, int o_dtype, const void* q, const void* k, cons
                    const float* descale, void* o, float* lse, int B, int H, int Hkv, int N, int d,
                    float scale, int causal, hipStream_t stream);
 
+// Wave-specialised bf16 forward (fa_fwd_ws.hip); arguments already validated.
+int launch_forward_ws(int o_dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                      int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
+
 // FP8 forward launch (descale: device pointer to {s_q, s_k, s_v}); inputs
 // E4M3 (e5m2 = 0) or E5M2 (e5m2 = 1); G = query heads per key/value head.
 hipError_t launch_forward_fp8(const void* q, const void* k, const void* v, const float* descale, void* o, float* lse,

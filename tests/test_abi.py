@@ -124,6 +124,35 @@ def test_forward_gqa_validation(kw, status):
     assert _fwd_gqa(**kw) == status
 
 
+def _fwd_ws(**kw):
+    a = dict(o_dtype=fa.FA_BF16, q=16, k=16, v=16, o=16, lse=16, B=1, H=8, Hkv=2, N=8, d=64, scale=0.125, causal=0)
+    a.update(kw)
+    return fa.lib().fa_forward_ws(a["o_dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                                  a["N"], a["d"], ctypes.c_float(a["scale"]), a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),   # does not divide H
+    (dict(Hkv=16), fa.FA_ERR_INVALID_ARG),  # more key/value heads than query heads
+    (dict(o_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_INVALID_ARG),
+    (dict(o_dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=24), fa.FA_ERR_INVALID_ARG),  # misaligned
+    (dict(H=0, Hkv=1), fa.FA_OK),
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None), fa.FA_OK),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),  # head larger than a 32-bit buffer range
+])
+def test_forward_ws_validation(kw, status):
+    assert _fwd_ws(**kw) == status
+
+
 def test_gqa_workspace_size():
     q_rows, kv_rows = 2 * 16 * 4096, 2 * 4 * 4096
     assert fa.fa_backward_gqa_workspace_bytes(2, 16, 4, 4096, 128) == \
