@@ -186,3 +186,34 @@ def test_deterministic():
     o1, l1 = gpu_forward_ws(inp, True)
     o2, l2 = gpu_forward_ws(inp, True)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_long_sequence_offsets():
+    """N = 2^20 + 77 (ragged), two heads, d=128, causal, float32 O: sampled
+    rows far into each head (both sides of 2^16 and 2^20, the last rows)
+    against the oracle, with the per-row relative bound of the long-sequence
+    test of the other kernels."""
+    from test_gpu_large import B, D, H, N, SEED, _relative, _rows
+    scale = 1.0 / math.sqrt(D)
+    rows = _rows()
+    print(f"case ws long sequence B={B} H={H} N={N} d={D} seed={SEED} rows/head={rows.shape[-1]}", flush=True)
+    inp = inputs.make_inputs(B, H, N, D, SEED, "bf16")
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+    fa.fa_forward_ws(fa.FA_F32, q, k, v, o, lse, scale, True)
+    torch.cuda.synchronize()
+    idx = torch.tensor(rows[0], device=dev)
+    pick = lambda t: torch.stack([t[0, h][idx[h]] for h in range(H)])[None].double().cpu().numpy()  # noqa: E731
+    g_o, g_lse = pick(o), pick(lse)
+    finite = bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    assert finite
+    cq, ck, cv = (inputs.to_numpy(inp[n]) for n in "qkv")
+    r_o, r_lse = oracle.forward(cq, ck, cv, scale, True, rows)
+    mx, rms = assert_close(g_o, r_o, "bf16", "O")
+    rel = _relative(g_o, r_o, "O", 2e-2)
+    le = assert_lse(g_lse, r_lse, "lse")
+    print(f"  O max={mx:.3g} rms={rms:.3g} of-allowed={rel:.3g} lse={le:.3g}", flush=True)
