@@ -217,3 +217,26 @@ def test_long_sequence_offsets():
     rel = _relative(g_o, r_o, "O", 2e-2)
     le = assert_lse(g_lse, r_lse, "lse")
     print(f"  O max={mx:.3g} rms={rms:.3g} of-allowed={rel:.3g} lse={le:.3g}", flush=True)
+
+
+def test_caller_stream():
+    """On a caller-made stream the results are the bits of the default-stream call."""
+    B, H, N, d = 2, 4, 777, 128
+    inp = inputs.make_inputs(B, H, N, d, 14, "bf16")
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in "qkv")
+    outs = []
+    for side in (False, True):
+        o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+        if side:
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            fa.fa_forward_ws(fa.FA_BF16, q, k, v, o, lse, 1.0 / math.sqrt(d), True, stream=st)
+            st.synchronize()
+        else:
+            fa.fa_forward_ws(fa.FA_BF16, q, k, v, o, lse, 1.0 / math.sqrt(d), True)
+            torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert bool(torch.isfinite(outs[0][0].float()).all())
